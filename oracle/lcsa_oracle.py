@@ -1,0 +1,231 @@
+"""CPU fp64 oracle for the LCSA forward pass (locality-constrained block-sparse causal attention).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this module. The product path (the HIP library and its Python binding) never calls it, and
+it shares no code with that path: the two meet only on the seeded input arrays.
+
+Source: "FlashVSR: Towards Real-time Diffusion-Based Streaming Video Super Resolution", the
+fmread pdfshare summary of the paper:
+  * sec. 2.2, Stage 2, causal masking: every latent attends only to the current and earlier times.
+  * sec. 2.2, Stage 2, block-sparse attention: Q and K are cut into non-overlapping blocks
+    (2x8x8 in the example), average-pooled to one feature per block, a coarse block-to-block
+    attention map is formed, the Top-K most relevant block pairs are kept and full attention runs
+    inside the kept blocks only.
+  * sec. 2.3, locality-constrained attention: at inference each query's attention is confined to a
+    local spatial neighbourhood (1152x1152 px in the example), with a "boundary-truncated" and a
+    "boundary-preserving" rule compared in sec. 3 (ablation, locality-constrained attention).
+The passages leave several steps open; the readings taken here (all stated in the design doc) are:
+  R1 causality is block-causal: key block j is visible from query block i iff its temporal block
+     index (latent frame // 2) is <= that of i; a block is fully visible inside the current one.
+  R2 Top-K is taken per query block over its visible key blocks, independently per (batch, head).
+  R3 K_i = min(topk, n_i) when a fixed topk is given, else clamp(floor(rho*n_i + 0.5), 1, n_i), with
+     n_i the number of visible key blocks; rho is the keep ratio (13.6% in the ablation).
+  R4 the coarse block map is the scaled dot product of the pooled vectors; a row softmax of it is
+     monotone and would not change the Top-K, so selection works on the logits.
+  R5 exact score ties go to the lower key-block index; no block is forced in.
+  R6 the window is block-granular and spatial only, w_b = win/8 blocks (odd), r = (w_b - 1)/2,
+     applied to the block rows and columns independently and identically in every visible
+     temporal block. Truncated: blocks within r of the query block, cut at the frame edge.
+     Preserving: a w_b-wide window slid inward at the edge, start = clamp(c - r, 0, N - w_b),
+     so every query keeps w_b blocks per axis when the grid has that many.
+  R7 the pooled feature is the arithmetic mean of the block's 128 tokens.
+Every function works in fp64 on exact copies of the kernel inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLK_T, BLK_H, BLK_W = 2, 8, 8
+BLK = BLK_T * BLK_H * BLK_W
+WIN_NONE, WIN_TRUNCATED, WIN_PRESERVING = 0, 1, 2
+
+
+# ----------------------------------------------------------------------------------- geometry
+def _grid(p):
+    hb, wb = p.grid_h // BLK_H, p.grid_w // BLK_W
+    return hb, wb
+
+
+def query_blocks(p):
+    """(tb, hb, wb) of every query block, in block-index order i = (tb_rel*Hb + hb)*Wb + wb.
+
+    tb is the ABSOLUTE temporal block (latent frame // 2); Q starts at latent frame q_frame0.
+    """
+    Hb, Wb = _grid(p)
+    out = []
+    for tr in range(p.q_frames // BLK_T):
+        for hb in range(Hb):
+            for wb in range(Wb):
+                out.append((p.q_frame0 // BLK_T + tr, hb, wb))
+    return out
+
+
+def key_blocks(p):
+    """(tb, hb, wb) of every key block, j = (tb*Hb + hb)*Wb + wb; K/V start at latent frame 0."""
+    Hb, Wb = _grid(p)
+    return [(tb, hb, wb) for tb in range(p.kv_frames // BLK_T) for hb in range(Hb) for wb in range(Wb)]
+
+
+def window_blocks(mode, c, n, wb_size):
+    """Set of block coordinates along one axis (of n blocks) that a query at block c may see (R6)."""
+    if mode == WIN_NONE:
+        return set(range(n))
+    r = (wb_size - 1) // 2
+    if mode == WIN_TRUNCATED:
+        return {x for x in range(n) if abs(x - c) <= r}
+    if mode == WIN_PRESERVING:
+        if n <= wb_size:
+            return set(range(n))
+        start = min(max(c - r, 0), n - wb_size)
+        return set(range(start, start + wb_size))
+    raise ValueError(mode)
+
+
+def visible(p):
+    """Boolean [nqb, nkb]: block-causal (R1) AND spatial window (R6), by enumeration."""
+    Hb, Wb = _grid(p)
+    qb, kb = query_blocks(p), key_blocks(p)
+    wh = p.win_h // BLK_H if p.win_mode != WIN_NONE else 0
+    ww = p.win_w // BLK_W if p.win_mode != WIN_NONE else 0
+    vis = np.zeros((len(qb), len(kb)), dtype=bool)
+    for i, (ti, hi, wi) in enumerate(qb):
+        rows = window_blocks(p.win_mode, hi, Hb, wh)
+        cols = window_blocks(p.win_mode, wi, Wb, ww)
+        for j, (tj, hj, wj) in enumerate(kb):
+            vis[i, j] = (tj <= ti) and (hj in rows) and (wj in cols)
+    return vis
+
+
+def keep_count(p, n: int) -> int:
+    """K_i for a row with n visible key blocks (R3); the ratio rule is evaluated in fp64."""
+    if p.topk > 0:
+        return min(p.topk, n)
+    x = float(p.keep_ratio) * float(n)
+    x = x + 0.5
+    return int(min(max(np.floor(x), 1), n))
+
+
+def csr_row_ptr(p, vis=None):
+    """row_ptr[nqb+1]: exclusive prefix sum of K_i (the same for every batch and head)."""
+    vis = visible(p) if vis is None else vis
+    k = [keep_count(p, int(n)) for n in vis.sum(axis=1)]
+    return np.concatenate([[0], np.cumsum(k)]).astype(np.int64)
+
+
+def block_tokens(p, blk, frame0):
+    """Token indices (raster order n = (t*H + h)*W + w) of block (tb, hb, wb) in a tensor whose
+    first latent frame is `frame0`."""
+    tb, hb, wb = blk
+    H, W = p.grid_h, p.grid_w
+    idx = []
+    for t in range(tb * BLK_T, tb * BLK_T + BLK_T):
+        for h in range(hb * BLK_H, hb * BLK_H + BLK_H):
+            for w in range(wb * BLK_W, wb * BLK_W + BLK_W):
+                idx.append(((t - frame0) * H + h) * W + w)
+    return np.array(idx, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------------- pooling
+def pool(p, x, which: str):
+    """Mean of each block's 128 tokens (R7). x: [B, heads, N, d] -> [B, heads, nblk, d] fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    blocks, f0 = (query_blocks(p), p.q_frame0) if which == "q" else (key_blocks(p), 0)
+    out = np.empty(x.shape[:2] + (len(blocks), x.shape[3]), dtype=np.float64)
+    for n, blk in enumerate(blocks):
+        out[:, :, n, :] = x[:, :, block_tokens(p, blk, f0), :].mean(axis=2)
+    return out
+
+
+# ------------------------------------------------------------------------- score + select
+def block_scores(p, qbar, kbar, vis=None):
+    """Coarse block map s_ij = scale * <qbar_i, kbar_j> (R4); -inf where j is not visible."""
+    vis = visible(p) if vis is None else vis
+    s = p.scale * np.matmul(qbar, np.swapaxes(kbar, -1, -2))
+    return np.where(vis[None, None], s, -np.inf)
+
+
+def select(p, scores, vis=None):
+    """Per (batch, head, query block): the K_i visible key blocks first in the order
+    (score descending, index ascending) (R2, R5); returned ascending in j, concatenated per row.
+
+    Returns (row_ptr [nqb+1], col_idx [B, heads, nnz]).
+    """
+    vis = visible(p) if vis is None else vis
+    row_ptr = csr_row_ptr(p, vis)
+    B, Hh, nqb, _ = scores.shape
+    col = np.empty((B, Hh, int(row_ptr[-1])), dtype=np.int64)
+    for b in range(B):
+        for h in range(Hh):
+            for i in range(nqb):
+                cand = np.flatnonzero(vis[i])
+                k = int(row_ptr[i + 1] - row_ptr[i])
+                order = np.lexsort((cand, -scores[b, h, i, cand]))  # primary: -score, then j
+                col[b, h, row_ptr[i]:row_ptr[i + 1]] = np.sort(cand[order[:k]])
+    return row_ptr, col
+
+
+# -------------------------------------------------------------------------------- attention
+def attend(p, q, k, v, row_ptr, col_idx, qblocks=None, bh=None):
+    """Exact softmax attention of every query token of block i over all tokens of the key blocks
+    listed for row i (no token-level mask inside a selected block).
+
+    q: [B, heads, Nq, d], k/v: [B, heads, Nk, d]. Returns O [B, heads, Nq, d] and lse [B, heads, Nq]
+    (natural log of the softmax denominator, max-shifted); rows not requested stay NaN.
+    qblocks: iterable of query-block indices to compute (default: all).
+    bh: iterable of (batch, head) pairs to compute (default: all).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hh, Nq, d = q.shape
+    qb, kb = query_blocks(p), key_blocks(p)
+    O = np.full(q.shape, np.nan)
+    lse = np.full(q.shape[:3], np.nan)
+    qblocks = range(len(qb)) if qblocks is None else qblocks
+    bh = [(b, h) for b in range(B) for h in range(Hh)] if bh is None else bh
+    ktok = [block_tokens(p, blk, 0) for blk in kb]
+    for i in qblocks:
+        qt = block_tokens(p, qb[i], p.q_frame0)
+        for b, h in bh:
+            sel = col_idx[b, h, row_ptr[i]:row_ptr[i + 1]]
+            kt = np.concatenate([ktok[j] for j in sel])
+            logits = p.scale * (q[b, h, qt] @ k[b, h, kt].T)      # [128, K_i*128]
+            m = logits.max(axis=1, keepdims=True)
+            e = np.exp(logits - m)
+            den = e.sum(axis=1, keepdims=True)
+            O[b, h, qt] = (e / den) @ v[b, h, kt]
+            lse[b, h, qt] = (m + np.log(den))[:, 0]
+    return O, lse
+
+
+def forward(p, q, k, v, qblocks=None, bh=None):
+    """The whole path: pool -> score -> mask -> Top-K -> exact attention on the kept blocks."""
+    vis = visible(p)
+    qbar, kbar = pool(p, q, "q"), pool(p, k, "k")
+    s = block_scores(p, qbar, kbar, vis)
+    row_ptr, col = select(p, s, vis)
+    O, lse = attend(p, q, k, v, row_ptr, col, qblocks=qblocks, bh=bh)
+    return dict(vis=vis, qbar=qbar, kbar=kbar, scores=s, row_ptr=row_ptr, col_idx=col, O=O, lse=lse)
+
+
+def dense_block_causal(p, q, k, v):
+    """Dense attention with the token mask induced by block visibility (every key token of a
+    visible block, no selection). With keep ratio 1 LCSA must reduce to this. Small inputs only."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    vis = visible(p)
+    Nq, Nk = q.shape[2], k.shape[2]
+    qblock_of = np.empty(Nq, dtype=np.int64)
+    kblock_of = np.empty(Nk, dtype=np.int64)
+    for i, blk in enumerate(query_blocks(p)):
+        qblock_of[block_tokens(p, blk, p.q_frame0)] = i
+    for j, blk in enumerate(key_blocks(p)):
+        kblock_of[block_tokens(p, blk, 0)] = j
+    mask = vis[qblock_of][:, kblock_of]                                # [Nq, Nk]
+    logits = p.scale * np.matmul(q, np.swapaxes(k, -1, -2))
+    logits = np.where(mask, logits, -np.inf)
+    m = logits.max(axis=-1, keepdims=True)
+    e = np.exp(logits - m)
+    den = e.sum(axis=-1, keepdims=True)
+    return np.matmul(e / den, v), (m + np.log(den))[..., 0]

@@ -1,0 +1,146 @@
+"""Pins for the oracle's pooling, block scores and Top-K selection.
+
+Pooling is pinned by closed forms (constant and affine fields) and by a reshape-based mean;
+selection by brute force: the rank definition, exhaustive search over subsets, and special cases.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from block_sparse_causal_lcsa_amd import workloads as W
+from oracle import lcsa_oracle as O
+
+
+def small(**kw):
+    base = dict(name="t", batch=2, heads=3, head_dim=8, grid_h=16, grid_w=24, kv_frames=4,
+                q_frame0=0, q_frames=4, dtype="f32", keep_ratio=0.3)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+# ------------------------------------------------------------------------------- pooling
+def coords(p, frame0, frames):
+    t, h, w = np.meshgrid(np.arange(frame0, frame0 + frames), np.arange(p.grid_h), np.arange(p.grid_w),
+                          indexing="ij")
+    return t.ravel().astype(float), h.ravel().astype(float), w.ravel().astype(float)
+
+
+@pytest.mark.parametrize("q0,qf,kvf", [(0, 4, 4), (2, 2, 6)])
+def test_pool_closed_forms(q0, qf, kvf):
+    p = small(q_frame0=q0, q_frames=qf, kv_frames=kvf)
+    rng = np.random.default_rng(7)
+    # block-constant input -> the mean is that constant (up to fp64 summation rounding)
+    qb = O.query_blocks(p)
+    const = rng.standard_normal((p.batch, p.heads, len(qb), p.head_dim))
+    t, h, w = coords(p, q0, qf)
+    blk_of = ((t // 2 - q0 // 2) * (p.grid_h // 8) + h // 8) * (p.grid_w // 8) + w // 8
+    x = const[:, :, blk_of.astype(int), :]
+    np.testing.assert_allclose(O.pool(p, x, "q"), const, rtol=1e-14, atol=0)
+    # affine field in (t, h, w) -> the value at the block centroid (t0 + 0.5, h0 + 3.5, w0 + 3.5)
+    a = rng.standard_normal((4, p.head_dim))
+    x = (a[0] + t[:, None] * a[1] + h[:, None] * a[2] + w[:, None] * a[3])[None, None]
+    x = np.broadcast_to(x, (1, 1) + x.shape[2:])
+    pooled = O.pool(p.replace(batch=1, heads=1), x, "q")[0, 0]
+    for i, (tb, hb, wb) in enumerate(qb):
+        centre = a[0] + (2 * tb + 0.5) * a[1] + (8 * hb + 3.5) * a[2] + (8 * wb + 3.5) * a[3]
+        np.testing.assert_allclose(pooled[i], centre, rtol=0, atol=1e-12)
+    # total mass: sum_i 128 * mean_i = sum over tokens
+    xk = rng.standard_normal((p.batch, p.heads, kvf * p.grid_h * p.grid_w, p.head_dim))
+    np.testing.assert_allclose(128 * O.pool(p, xk, "k").sum(axis=2), xk.sum(axis=2), rtol=1e-13, atol=1e-11)
+
+
+def test_pool_matches_reshape_mean():
+    p = small(kv_frames=6)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((p.batch, p.heads, 6 * 16 * 24, p.head_dim))
+    # [B, Hh, T/2, 2, Hb, 8, Wb, 8, d] -> mean over the three intra-block axes
+    r = x.reshape(p.batch, p.heads, 3, 2, 2, 8, 3, 8, p.head_dim).mean(axis=(3, 5, 7))
+    r = r.reshape(p.batch, p.heads, 3 * 2 * 3, p.head_dim)
+    np.testing.assert_allclose(O.pool(p, x, "k"), r, rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------ selection
+def brute_rank_select(s, cand, k):
+    """Selected iff fewer than k candidates come before it in (score desc, index asc)."""
+    sel = []
+    for j in cand:
+        rank = sum(1 for jj in cand if s[jj] > s[j] or (s[jj] == s[j] and jj < j))
+        if rank < k:
+            sel.append(j)
+    return sorted(sel)
+
+
+@pytest.mark.parametrize("mode", [O.WIN_NONE, O.WIN_TRUNCATED, O.WIN_PRESERVING])
+@pytest.mark.parametrize("quantise", [False, True])
+def test_select_matches_rank_definition(mode, quantise):
+    kw = dict(win_mode=mode, win_h=24, win_w=24) if mode else {}
+    p = small(grid_h=40, grid_w=32, kv_frames=6, q_frame0=2, q_frames=4, **kw)
+    rng = np.random.default_rng(11)
+    vis = O.visible(p)
+    s = rng.standard_normal((p.batch, p.heads) + vis.shape)
+    if quantise:                       # many exact ties: the lower index must win
+        s = np.round(s * 2) / 2
+    s = np.where(vis, s, -np.inf)
+    rp, col = O.select(p, s, vis)
+    for b in range(p.batch):
+        for h in range(p.heads):
+            for i in range(vis.shape[0]):
+                cand = list(np.flatnonzero(vis[i]))
+                k = int(rp[i + 1] - rp[i])
+                assert k == O.keep_count(p, len(cand))
+                got = list(col[b, h, rp[i]:rp[i + 1]])
+                assert got == brute_rank_select(s[b, h, i], cand, k)
+
+
+def test_select_exhaustive_subsets():
+    """For distinct scores the kept set is the K-subset with the largest total score."""
+    rng = np.random.default_rng(5)
+    for n in range(1, 11):
+        for k in range(1, n + 1):
+            s = rng.standard_normal(n)
+            best = max(itertools.combinations(range(n), k), key=lambda c: s[list(c)].sum())
+            p = W.Workload("x", 1, 1, 8, 8, 8 * n, 2, 0, 2, dtype="f32", topk=k)
+            vis = O.visible(p)          # 1 query block sees all n blocks of its temporal block
+            assert vis.shape == (n, n) and vis.all()
+            rp, col = O.select(p, np.broadcast_to(s, (1, 1, n, n)), vis)
+            assert list(col[0, 0, :k]) == sorted(best)
+
+
+def test_select_special_cases():
+    p = small(q_frame0=2, q_frames=2, kv_frames=4, keep_ratio=1.0)
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((p.batch, p.heads, 2 * 16 * 24, p.head_dim))
+    k = rng.standard_normal((p.batch, p.heads, 4 * 16 * 24, p.head_dim))
+    vis = O.visible(p)
+    # keep ratio 1: every visible block is kept
+    rp, col = O.select(p, O.block_scores(p, O.pool(p, q, "q"), O.pool(p, k, "k"), vis), vis)
+    for i in range(vis.shape[0]):
+        assert list(col[0, 0, rp[i]:rp[i + 1]]) == list(np.flatnonzero(vis[i]))
+    # constant key features: all scores in a row tie, so the K_i lowest visible indices win
+    p2 = p.replace(keep_ratio=0.25)
+    kc = np.ones_like(k)
+    rp, col = O.select(p2, O.block_scores(p2, O.pool(p2, q, "q"), O.pool(p2, kc, "k"), vis), vis)
+    for i in range(vis.shape[0]):
+        n = int(rp[i + 1] - rp[i])
+        assert list(col[1, 2, rp[i]:rp[i + 1]]) == list(np.flatnonzero(vis[i])[:n])
+    # a positive rescale of Q changes no selection; the selection never leaves the visible set
+    s1 = O.block_scores(p2, O.pool(p2, q, "q"), O.pool(p2, k, "k"), vis)
+    s2 = O.block_scores(p2, O.pool(p2, 3.0 * q, "q"), O.pool(p2, k, "k"), vis)
+    _, c1 = O.select(p2, s1, vis)
+    rp, c2 = O.select(p2, s2, vis)
+    assert np.array_equal(c1, c2)
+    for i in range(vis.shape[0]):
+        assert vis[i, c1[:, :, rp[i]:rp[i + 1]]].all()
+
+
+def test_scores_match_einsum():
+    p = small()
+    rng = np.random.default_rng(2)
+    qb = rng.standard_normal((p.batch, p.heads, 12, p.head_dim))
+    kb = rng.standard_normal((p.batch, p.heads, 12, p.head_dim))
+    vis = O.visible(p)
+    s = O.block_scores(p, qb, kb, vis)
+    ref = np.einsum("bhid,bhjd->bhij", qb, kb) * p.scale
+    assert np.allclose(s[:, :, vis], ref[:, :, vis], rtol=1e-14, atol=1e-14)
+    assert np.all(np.isneginf(s[:, :, ~vis]))

@@ -1,0 +1,57 @@
+"""Builds liblcsa.so (the C-ABI library) in-tree with hipcc for gfx950.
+
+    python -m block_sparse_causal_lcsa_amd.build
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "liblcsa.so")
+ARCH = "gfx950"
+
+KERNELS = ["pool.hip", "score_select.hip", "attn_fwd.hip"]
+HOST = ["lcsa_host.cpp"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# Packed fp32 VALU ops are kept out of every device build.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-munsafe-fp-atomics"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OUT, exist_ok=True)
+    jobs = []
+    for src in KERNELS:
+        obj = os.path.join(OUT, src.replace(".hip", ".o"))
+        jobs.append(["hipcc", *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in HOST:
+        obj = os.path.join(OUT, src.replace(".cpp", ".o"))
+        # host only; fp64 keep-ratio rule evaluated without contraction
+        jobs.append(["hipcc", *COMMON, "-ffp-contract=off", "-c", os.path.join(CSRC, src), "-o", obj])
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        for out in ex.map(_run, jobs):
+            if verbose and out.strip():
+                print(out)
+    objs = [j[-1] for j in jobs]
+    tmp = LIB + ".tmp"
+    _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

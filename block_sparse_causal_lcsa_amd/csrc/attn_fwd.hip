@@ -1,0 +1,336 @@
+// lcsa_attn_fwd: exact softmax attention of each 128-token query block over the tokens of its kept
+// key blocks (FlashVSR summary, sec. 2.2: full attention is applied inside the selected blocks only).
+//
+// One workgroup (4 waves, 256 lanes) per (batch, head, query block); wave w owns query rows
+// 32w..32w+31 of the block. For every kept key block j (128 tokens):
+//   - K_j is staged in LDS row-major [key][d] and V_j transposed [d][key] (bf16), from registers that
+//     were loaded from HBM/L2 while the previous block was being computed;
+//   - S^T = K_j Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the wave's Q rows held in
+//     registers). In the result each lane holds one query row (lane % 32) and half of the key
+//     columns, so the online softmax needs one cross-lane max per block and no other exchange;
+//   - the scores become P = exp2(S * scale * log2(e) - m) in fp32 (running max m, running sum l),
+//     P is rounded to bf16 and used directly as the B operand of O^T += V_j^T P^T: the k-order of
+//     the PV MFMA is permuted to match the score layout, and V^T is read from LDS in that order.
+// At the end O = O / l (bf16 RNE or fp32) and lse = ln(sum exp(scale q.k)) in fp32.
+// Workgroup ids are remapped so that consecutive query blocks of one head run on the same XCD,
+// whose L2 then serves the key blocks that neighbouring query blocks share.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "lcsa_internal.h"
+
+namespace lcsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;           // [B*Hh, Nq] or null
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t qsb, qsh, qst, ksb, ksh, kst, vsb, vsh, vst, osb, osh, ost;
+  Geom g;
+  int32_t heads;
+  int32_t nnz;
+  int32_t nq_tok;       // query tokens per (batch, head)
+  int32_t nwg;
+  float c;              // scale * log2(e)
+};
+
+constexpr int kBN = 128;  // keys per kept block
+constexpr int kPadK = 8;  // bf16 elements of padding per LDS row
+
+// Token index (within its tensor) of row r (0..127) of block (tr, hb, wb), tr relative to the
+// tensor's first temporal block.
+__device__ __forceinline__ int64_t block_token(const Geom& g, int tr, int hb, int wb, int r) {
+  return (int64_t(kBlkT * tr + (r >> 6)) * g.H + kBlkH * hb + ((r >> 3) & 7)) * g.W + kBlkW * wb + (r & 7);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)lo)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)hi)) << 16);
+}
+
+// Per-thread staging registers for one key block.
+template <typename T, int D>
+struct Stage {
+  static constexpr int KCH = kBN * D / 8 / 256;  // 16-byte bf16 chunks of K per lane
+  static constexpr int VGRP = 128 / D;           // 8-key groups per wave instruction set
+  static constexpr int VIT = kBN / 8 / 4 / VGRP; // 8-key units per lane
+  // K: 8 consecutive d of one key per chunk; V: 2 consecutive d of 8 consecutive keys per unit
+  uint32_t k[KCH][4];
+  uint32_t v[VIT][8];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void stage_load(Stage<T, D>& st, const T* kb, const T* vb, int64_t kst, int64_t vst,
+                                           const Geom& g, int j) {
+  const int tr = j / g.bpt, rem = j - (j / g.bpt) * g.bpt;
+  const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
+  const int t = threadIdx.x;
+  constexpr int CPR = D / 8;  // 8-element chunks per key row
+#pragma unroll
+  for (int it = 0; it < Stage<T, D>::KCH; ++it) {
+    const int id = t + 256 * it;
+    const int r = id / CPR, c = id % CPR;
+    const T* src = kb + block_token(g, tr, hb, wb, r) * kst + 8 * c;
+    if constexpr (sizeof(T) == 2) {
+      const uint4 x = *reinterpret_cast<const uint4*>(src);
+      st.k[it][0] = x.x; st.k[it][1] = x.y; st.k[it][2] = x.z; st.k[it][3] = x.w;
+    } else {
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      st.k[it][0] = pack_bf16x2(x0.x, x0.y); st.k[it][1] = pack_bf16x2(x0.z, x0.w);
+      st.k[it][2] = pack_bf16x2(x1.x, x1.y); st.k[it][3] = pack_bf16x2(x1.z, x1.w);
+    }
+  }
+  const int wave = t >> 6, lane = t & 63;
+  const int dl = lane % (D / 2);        // d pair index
+  const int grp = lane / (D / 2);       // which of the VGRP key groups this lane serves
+#pragma unroll
+  for (int u = 0; u < Stage<T, D>::VIT; ++u) {
+    const int r0 = 8 * ((wave * Stage<T, D>::VIT + u) * Stage<T, D>::VGRP + grp);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const T* src = vb + block_token(g, tr, hb, wb, r0 + e) * vst + 2 * dl;
+      if constexpr (sizeof(T) == 2) {
+        st.v[u][e] = *reinterpret_cast<const uint32_t*>(src);
+      } else {
+        const float2 x = *reinterpret_cast<const float2*>(src);
+        st.v[u][e] = pack_bf16x2(x.x, x.y);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void stage_store(const Stage<T, D>& st, uint16_t* Ks, uint16_t* Vt) {
+  constexpr int KP = D + kPadK, VP = kBN + kPadK;
+  constexpr int CPR = D / 8;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < Stage<T, D>::KCH; ++it) {
+    const int id = t + 256 * it;
+    const int r = id / CPR, c = id % CPR;
+    *reinterpret_cast<uint4*>(Ks + r * KP + 8 * c) = make_uint4(st.k[it][0], st.k[it][1], st.k[it][2], st.k[it][3]);
+  }
+  const int wave = t >> 6, lane = t & 63;
+  const int dl = lane % (D / 2);
+  const int grp = lane / (D / 2);
+#pragma unroll
+  for (int u = 0; u < Stage<T, D>::VIT; ++u) {
+    const int r0 = 8 * ((wave * Stage<T, D>::VIT + u) * Stage<T, D>::VGRP + grp);
+    const uint32_t* w = st.v[u];
+    // low halves -> row d = 2*dl, high halves -> row 2*dl + 1; 8 consecutive keys each
+    const uint4 lo = make_uint4(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u),
+                                __builtin_amdgcn_perm(w[5], w[4], 0x05040100u), __builtin_amdgcn_perm(w[7], w[6], 0x05040100u));
+    const uint4 hi = make_uint4(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u),
+                                __builtin_amdgcn_perm(w[5], w[4], 0x07060302u), __builtin_amdgcn_perm(w[7], w[6], 0x07060302u));
+    *reinterpret_cast<uint4*>(Vt + (2 * dl) * VP + r0) = lo;
+    *reinterpret_cast<uint4*>(Vt + (2 * dl + 1) * VP + r0) = hi;
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
+  constexpr int KP = D + kPadK, VP = kBN + kPadK;
+  constexpr int DS = D / 16;  // 16-wide d steps of the QK^T MFMA
+  constexpr int DT = D / 32;  // 32-wide d tiles of the output
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+
+  const Geom& g = a.g;
+  // XCD-aware order: hardware deals workgroup n to XCD n % 8; give each XCD a contiguous range
+  int wg = blockIdx.x;
+  const int n8 = (a.nwg / 8) * 8;
+  if (wg < n8) wg = (wg % 8) * (a.nwg / 8) + wg / 8;
+  const int bh = wg / g.nqb, i = wg - (wg / g.nqb) * g.nqb;
+  const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
+
+  const T* qb = static_cast<const T*>(a.q) + b * a.qsb + h * a.qsh;
+  const T* kb = static_cast<const T*>(a.k) + b * a.ksb + h * a.ksh;
+  const T* vb = static_cast<const T*>(a.v) + b * a.vsb + h * a.vsh;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
+  const int qhb = qrem / g.Wb, qwb = qrem - (qrem / g.Wb) * g.Wb;
+  const int64_t qtok = block_token(g, qtr, qhb, qwb, 32 * wave + l32);
+
+  // B operand of S^T = K Q^T: lane holds Q[row l32][16*s + 8*hi + 0..7]
+  bf16x8 qf[DS];
+  {
+    const T* src = qb + qtok * a.qst + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      if constexpr (sizeof(T) == 2) {
+        qf[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
+      } else {
+        const float4 x0 = *reinterpret_cast<const float4*>(src + 16 * s);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + 16 * s + 4);
+        qf[s] = bf16x8{(__bf16)x0.x, (__bf16)x0.y, (__bf16)x0.z, (__bf16)x0.w,
+                       (__bf16)x1.x, (__bf16)x1.y, (__bf16)x1.z, (__bf16)x1.w};
+      }
+    }
+  }
+
+  const int beg = a.row_ptr[i], nsel = a.row_ptr[i + 1] - beg;
+  const int32_t* sel = a.col_idx + int64_t(bh) * a.nnz + beg;
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  Stage<T, D> st;
+  int jn = nsel > 0 ? sel[0] : 0;
+  bool ok_next = jn >= 0 && jn < g.nkb;
+  if (nsel > 0) stage_load<T, D>(st, kb, vb, a.kst, a.vst, g, ok_next ? jn : 0);
+
+  for (int n = 0; n < nsel; ++n) {
+    const bool ok = ok_next;
+    __syncthreads();  // every wave is done reading the previous block
+    stage_store<T, D>(st, Ks, Vt);
+    __syncthreads();
+    if (n + 1 < nsel) {
+      jn = sel[n + 1];
+      ok_next = jn >= 0 && jn < g.nkb;
+      stage_load<T, D>(st, kb, vb, a.kst, a.vst, g, ok_next ? jn : 0);
+    }
+    if (!ok) continue;
+
+    // S^T tiles: 4 x (32 keys x 32 queries)
+    f32x16 sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      sacc[kt] = f32x16{};
+      const uint16_t* kr = Ks + (kt * 32 + l32) * KP + 8 * hi;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
+      }
+    }
+    // online softmax in the log2 domain; this lane holds 64 of the row's 128 scores
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sacc[kt][v] *= a.c;
+        mx = fmaxf(mx, sacc[kt][v]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float ls = 0.f;
+    bf16x8 pf[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(sacc[kt][8 * h2 + e] - m_new);
+          ls += pv;
+          pf[kt][h2][e] = (__bf16)pv;
+        }
+    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+
+    // O^T += V^T P^T. MFMA k-slot 8*hi + e of step (kt, h2) is key kt*32 + 16*h2 + 8*(e/4) + 4*hi + e%4,
+    // which is where the score layout put P; V^T is read in the same order (two 4-key runs).
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* vr = Vt + (dt * 32 + l32) * VP + 4 * hi;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vr + kt * 32 + 16 * h2);
+          const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vr + kt * 32 + 16 * h2 + 8);
+          const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kt][h2], oacc[dt], 0, 0, 0);
+        }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  T* ob = static_cast<T*>(a.o) + b * a.osb + h * a.osh + block_token(g, qtr, qhb, qwb, 32 * wave + l32) * a.ost;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      // items 4*g4..4*g4+3 are d = dt*32 + 8*g4 + 4*hi + 0..3
+      const int d0 = dt * 32 + 8 * g4 + 4 * hi;
+      const float o0 = oacc[dt][4 * g4] * inv, o1 = oacc[dt][4 * g4 + 1] * inv;
+      const float o2 = oacc[dt][4 * g4 + 2] * inv, o3 = oacc[dt][4 * g4 + 3] * inv;
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint2*>(ob + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+      } else {
+        *reinterpret_cast<float4*>(ob + d0) = make_float4(o0, o1, o2, o3);
+      }
+    }
+  if (a.lse && hi == 0) {
+    const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    a.lse[int64_t(bh) * a.nq_tok + block_token(g, qtr, qhb, qwb, 32 * wave + l32)] = lse;
+  }
+}
+
+}  // namespace
+}  // namespace lcsa
+
+using namespace lcsa;
+
+extern "C" lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
+                                     lcsa_strides ks, const void* v, lcsa_strides vs, const int32_t* row_ptr,
+                                     const int32_t* col_idx, void* o, lcsa_strides os, float* lse, void* stream) {
+  Geom g;
+  lcsa_status st = validate_problem(p, &g);
+  if (st != LCSA_OK) return st;
+  const int64_t hw = int64_t(p->grid_h) * p->grid_w;
+  if ((st = check_tensor("q", q, qs, p, hw * p->q_frames)) != LCSA_OK) return st;
+  if ((st = check_tensor("k", k, ks, p, hw * p->kv_frames)) != LCSA_OK) return st;
+  if ((st = check_tensor("v", v, vs, p, hw * p->kv_frames)) != LCSA_OK) return st;
+  if ((st = check_tensor("o", o, os, p, hw * p->q_frames)) != LCSA_OK) return st;
+  if (!row_ptr || !col_idx) return fail(LCSA_ERR_INVALID, "lcsa_attn_fwd: row_ptr or col_idx is NULL");
+  if (reinterpret_cast<uintptr_t>(row_ptr) % 4 || reinterpret_cast<uintptr_t>(col_idx) % 4 ||
+      reinterpret_cast<uintptr_t>(lse) % 4)
+    return fail(LCSA_ERR_INVALID, "lcsa_attn_fwd: misaligned row_ptr, col_idx or lse");
+  int32_t nnz = 0;
+  if ((st = lcsa_csr_layout(p, nullptr, nullptr, &nnz, nullptr)) != LCSA_OK) return st;
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.qsb = qs.batch; a.qsh = qs.head; a.qst = qs.token;
+  a.ksb = ks.batch; a.ksh = ks.head; a.kst = ks.token;
+  a.vsb = vs.batch; a.vsh = vs.head; a.vst = vs.token;
+  a.osb = os.batch; a.osh = os.head; a.ost = os.token;
+  a.g = g;
+  a.heads = p->heads;
+  a.nnz = nnz;
+  a.nq_tok = static_cast<int32_t>(hw * p->q_frames);
+  a.nwg = p->batch * p->heads * g.nqb;
+  a.c = static_cast<float>(static_cast<double>(p->scale) * 1.4426950408889634);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (p->dtype == LCSA_BF16) {
+    if (p->head_dim == 128) attn_fwd_kernel<uint16_t, 128><<<a.nwg, 256, 0, s>>>(a);
+    else attn_fwd_kernel<uint16_t, 64><<<a.nwg, 256, 0, s>>>(a);
+  } else {
+    if (p->head_dim == 128) attn_fwd_kernel<float, 128><<<a.nwg, 256, 0, s>>>(a);
+    else attn_fwd_kernel<float, 64><<<a.nwg, 256, 0, s>>>(a);
+  }
+  return hip_status(hipGetLastError(), "lcsa_attn_fwd launch");
+}

@@ -1,0 +1,83 @@
+// Block geometry of an LCSA problem, shared by the host layer and the kernels.
+//
+// Blocks are 2x8x8 tokens (t x h x w). Block-causal visibility follows FlashVSR's stage-2 causal
+// masking (fmread summary, sec. 2.2): key block j is visible from query block i iff its temporal
+// block (latent frame / 2) is not later than i's. The locality window of sec. 2.3 is applied per
+// spatial axis at block granularity: w_b = win / 8 blocks (odd), r = (w_b - 1) / 2;
+//   truncated:  [c - r, c + r] cut to [0, n)
+//   preserving: a w_b-wide window slid inward at the frame edge, start = clamp(c - r, 0, n - w_b).
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define LCSA_HD __host__ __device__ __forceinline__
+#else
+#define LCSA_HD inline
+#endif
+
+namespace lcsa {
+
+constexpr int kBlkT = 2, kBlkH = 8, kBlkW = 8;
+constexpr int kBlkTokens = kBlkT * kBlkH * kBlkW;  // 128
+
+struct Geom {
+  int32_t H, W;          // tokens per frame
+  int32_t Hb, Wb;        // blocks per frame
+  int32_t bpt;           // blocks per temporal block = Hb * Wb
+  int32_t nqb, nkb;      // query / key blocks per (batch, head)
+  int32_t q_tb0;         // absolute temporal block of query block 0 (q_frame0 / 2)
+  int32_t win_mode;      // 0 none, 1 truncated, 2 preserving
+  int32_t wbh, wbw;      // window width in blocks per axis (odd), when win_mode != 0
+};
+
+// Inclusive block range [lo, hi] visible along one axis of n blocks from block c.
+LCSA_HD void win_range(int mode, int c, int n, int wb, int* lo, int* hi) {
+  if (mode == 0 || wb >= 2 * n - 1) {
+    *lo = 0;
+    *hi = n - 1;
+    return;
+  }
+  const int r = (wb - 1) / 2;
+  if (mode == 1) {
+    *lo = c - r < 0 ? 0 : c - r;
+    *hi = c + r > n - 1 ? n - 1 : c + r;
+  } else {
+    if (n <= wb) {
+      *lo = 0;
+      *hi = n - 1;
+      return;
+    }
+    int s = c - r;
+    s = s < 0 ? 0 : s;
+    s = s > n - wb ? n - wb : s;
+    *lo = s;
+    *hi = s + wb - 1;
+  }
+}
+
+// Absolute temporal block, block row and block column of query block i.
+LCSA_HD void qblock_coords(const Geom& g, int i, int* tb, int* hb, int* wb) {
+  const int tr = i / g.bpt, rem = i - tr * g.bpt;
+  *tb = g.q_tb0 + tr;
+  *hb = rem / g.Wb;
+  *wb = rem - (rem / g.Wb) * g.Wb;
+}
+
+// Visible spatial window of query block i: block rows [h0, h1], block columns [w0, w1];
+// returns the last visible temporal block.
+LCSA_HD int qblock_window(const Geom& g, int i, int* h0, int* h1, int* w0, int* w1) {
+  int tb, hb, wb;
+  qblock_coords(g, i, &tb, &hb, &wb);
+  win_range(g.win_mode, hb, g.Hb, g.wbh, h0, h1);
+  win_range(g.win_mode, wb, g.Wb, g.wbw, w0, w1);
+  return tb;
+}
+
+LCSA_HD int n_visible(const Geom& g, int i) {
+  int h0, h1, w0, w1;
+  const int tb = qblock_window(g, i, &h0, &h1, &w0, &w1);
+  return (tb + 1) * (h1 - h0 + 1) * (w1 - w0 + 1);
+}
+
+}  // namespace lcsa

@@ -1,0 +1,207 @@
+"""Thin Python binding of liblcsa.so (ctypes). Argument marshalling only: every step of the LCSA
+forward runs in the library's HIP kernels; torch provides device memory and the stream.
+
+The functions carry the C names: lcsa_csr_layout, lcsa_pool, lcsa_score_select, lcsa_attn_fwd.
+`forward` chains the three device calls on the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblcsa.so")
+
+LCSA_OK, LCSA_ERR_INVALID, LCSA_ERR_UNSUPPORTED, LCSA_ERR_HIP = 0, 1, 2, 3
+LCSA_BF16, LCSA_F32 = 0, 1
+
+EXPORTS = ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
+           "lcsa_status_string", "lcsa_last_error", "lcsa_version")
+
+
+class LcsaProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "heads", "head_dim", "grid_h", "grid_w", "kv_frames", "q_frame0", "q_frames",
+        "blk_t", "blk_h", "blk_w", "win_mode", "win_h", "win_w", "topk")] + [
+        ("keep_ratio", ctypes.c_double), ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class LcsaStrides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
+class LcsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Loads liblcsa.so; raises if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m block_sparse_causal_lcsa_amd.build` (or __graft_entry__.build())")
+    # The library must run on the same HIP runtime instance that owns the caller's device memory
+    # and streams. torch ships its own libamdhip64; importing torch first makes the dynamic loader
+    # bind liblcsa.so to that instance (same soname) instead of mapping a second runtime.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    P, S, vp = ctypes.POINTER(LcsaProblem), LcsaStrides, ctypes.c_void_p
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.lcsa_csr_layout.argtypes = [P, i32p, i32p, i32p, i32p]
+    lib.lcsa_pool.argtypes = [P, vp, S, vp, S, vp, vp, vp]
+    lib.lcsa_score_select.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.lcsa_attn_fwd.argtypes = [P, vp, S, vp, S, vp, S, vp, vp, vp, S, vp, vp]
+    for f in ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.lcsa_status_string.argtypes = [ctypes.c_int]
+    lib.lcsa_status_string.restype = ctypes.c_char_p
+    lib.lcsa_last_error.argtypes = []
+    lib.lcsa_last_error.restype = ctypes.c_char_p
+    lib.lcsa_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _status_name(s: int) -> str:
+    return {0: "LCSA_OK", 1: "LCSA_ERR_INVALID", 2: "LCSA_ERR_UNSUPPORTED", 3: "LCSA_ERR_HIP"}.get(s, str(s))
+
+
+def _check(status: int):
+    if status != LCSA_OK:
+        raise LcsaError(status, load().lcsa_last_error().decode())
+
+
+def problem(w) -> LcsaProblem:
+    """LcsaProblem from any object with the Workload attributes."""
+    return LcsaProblem(batch=w.batch, heads=w.heads, head_dim=w.head_dim, grid_h=w.grid_h, grid_w=w.grid_w,
+                       kv_frames=w.kv_frames, q_frame0=w.q_frame0, q_frames=w.q_frames, blk_t=w.blk_t,
+                       blk_h=w.blk_h, blk_w=w.blk_w, win_mode=w.win_mode, win_h=w.win_h, win_w=w.win_w,
+                       topk=w.topk, keep_ratio=w.keep_ratio, scale=w.scale,
+                       dtype=LCSA_F32 if w.dtype == "f32" else LCSA_BF16)
+
+
+def lcsa_csr_layout(p: LcsaProblem):
+    """Returns (nqb, nkb, nnz_per_head, row_ptr int32 numpy [nqb+1]); host only."""
+    lib = load()
+    nqb, nkb, nnz = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.lcsa_csr_layout(ctypes.byref(p), ctypes.byref(nqb), ctypes.byref(nkb), ctypes.byref(nnz), None))
+    rp = np.zeros(nqb.value + 1, dtype=np.int32)
+    _check(lib.lcsa_csr_layout(ctypes.byref(p), None, None, None,
+                               rp.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return nqb.value, nkb.value, nnz.value, rp
+
+
+# ------------------------------------------------------------------------------- device calls
+def _torch():
+    import torch
+    return torch
+
+
+def _strides(t) -> LcsaStrides:
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("token tensors must be [batch, heads, tokens, head_dim] with unit head_dim stride")
+    return LcsaStrides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype(p: LcsaProblem):
+    torch = _torch()
+    return torch.float32 if p.dtype == LCSA_F32 else torch.bfloat16
+
+
+def _check_token_tensor(name, t, p, ntok):
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != _dtype(p):
+        raise ValueError(f"{name} has dtype {t.dtype}, problem expects {_dtype(p)}")
+    if tuple(t.shape) != (p.batch, p.heads, ntok, p.head_dim):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(p.batch, p.heads, ntok, p.head_dim)}")
+    return torch
+
+
+def lcsa_pool(p: LcsaProblem, q, k, q_pooled=None, k_pooled=None, stream=None):
+    """Block means of q and k (either may be None) -> (q_pooled, k_pooled) fp32 device tensors."""
+    torch = _torch()
+    nqb, nkb, _, _ = lcsa_csr_layout(p)
+    hw = p.grid_h * p.grid_w
+    if q is not None:
+        _check_token_tensor("q", q, p, p.q_frames * hw)
+        if q_pooled is None:
+            q_pooled = torch.empty((p.batch, p.heads, nqb, p.head_dim), dtype=torch.float32, device=q.device)
+    if k is not None:
+        _check_token_tensor("k", k, p, p.kv_frames * hw)
+        if k_pooled is None:
+            k_pooled = torch.empty((p.batch, p.heads, nkb, p.head_dim), dtype=torch.float32, device=k.device)
+    zs = LcsaStrides(0, 0, 0)
+    _check(load().lcsa_pool(ctypes.byref(p), _ptr(q), _strides(q) if q is not None else zs, _ptr(k),
+                            _strides(k) if k is not None else zs, _ptr(q_pooled if q is not None else None),
+                            _ptr(k_pooled if k is not None else None), _stream(stream)))
+    return q_pooled, k_pooled
+
+
+def lcsa_score_select(p: LcsaProblem, q_pooled, k_pooled, row_ptr, col_idx=None, scores_dbg=None, stream=None):
+    """Per-row Top-K key blocks -> col_idx int32 [B, Hh, nnz_per_head] (row_ptr: device int32)."""
+    torch = _torch()
+    nqb, nkb, nnz, _ = lcsa_csr_layout(p)
+    for name, t, n in (("q_pooled", q_pooled, nqb), ("k_pooled", k_pooled, nkb)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (p.batch, p.heads, n, p.head_dim):
+            raise ValueError(f"{name} must be contiguous fp32 [{p.batch}, {p.heads}, {n}, {p.head_dim}]")
+    if row_ptr.dtype != torch.int32 or row_ptr.numel() != nqb + 1 or not row_ptr.is_cuda:
+        raise ValueError("row_ptr must be a device int32 tensor of nqb + 1 entries")
+    if col_idx is None:
+        col_idx = torch.empty((p.batch, p.heads, nnz), dtype=torch.int32, device=q_pooled.device)
+    if scores_dbg is not None and (scores_dbg.dtype != torch.float64 or not scores_dbg.is_contiguous()
+                                   or scores_dbg.numel() != p.batch * p.heads * nqb * nkb):
+        raise ValueError("scores_dbg must be contiguous fp64 [B, Hh, nqb, nkb]")
+    _check(load().lcsa_score_select(ctypes.byref(p), _ptr(q_pooled), _ptr(k_pooled), _ptr(row_ptr), _ptr(col_idx),
+                                    _ptr(scores_dbg), _stream(stream)))
+    return col_idx
+
+
+def lcsa_attn_fwd(p: LcsaProblem, q, k, v, row_ptr, col_idx, o=None, lse=None, want_lse=True, stream=None):
+    """Exact attention over the kept blocks -> (o, lse)."""
+    torch = _torch()
+    hw = p.grid_h * p.grid_w
+    _check_token_tensor("q", q, p, p.q_frames * hw)
+    _check_token_tensor("k", k, p, p.kv_frames * hw)
+    _check_token_tensor("v", v, p, p.kv_frames * hw)
+    if o is None:
+        o = torch.empty_like(q)
+    _check_token_tensor("o", o, p, p.q_frames * hw)
+    if lse is None and want_lse:
+        lse = torch.empty((p.batch, p.heads, p.q_frames * hw), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous fp32 [B, Hh, Nq]")
+    _check(load().lcsa_attn_fwd(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                _ptr(row_ptr), _ptr(col_idx), _ptr(o), _strides(o), _ptr(lse), _stream(stream)))
+    return o, lse
+
+
+def forward(p: LcsaProblem, q, k, v, row_ptr=None, stream=None):
+    """pool -> score_select -> attn_fwd on one stream. Returns a dict of device tensors."""
+    torch = _torch()
+    if row_ptr is None:
+        row_ptr = torch.from_numpy(lcsa_csr_layout(p)[3]).to(q.device)
+    qp, kp = lcsa_pool(p, q, k, stream=stream)
+    col = lcsa_score_select(p, qp, kp, row_ptr, stream=stream)
+    o, lse = lcsa_attn_fwd(p, q, k, v, row_ptr, col, stream=stream)
+    return dict(q_pooled=qp, k_pooled=kp, row_ptr=row_ptr, col_idx=col, o=o, lse=lse)

@@ -1,0 +1,121 @@
+/*
+ * lcsa.h - C ABI of liblcsa.so: locality-constrained block-sparse causal attention (LCSA)
+ * forward on AMD MI355X (gfx950).
+ *
+ * The operation is the one described for FlashVSR's stage-2 sparse-causal attention and its
+ * locality-constrained inference ("FlashVSR: Towards Real-time Diffusion-Based Streaming Video
+ * Super Resolution", fmread pdfshare summary, sec. 2.2 "Stage 2: block-sparse causal attention
+ * adaptation" and sec. 2.3 "locality-constrained sparse attention"):
+ *   1. Q and K are cut into non-overlapping spatio-temporal blocks of blk_t x blk_h x blk_w tokens
+ *      (2x8x8) and each block is average-pooled to one feature vector      -> lcsa_pool
+ *   2. a coarse block-to-block map s_ij = scale * <qbar_i, kbar_j> is scored over the key blocks
+ *      that query block i may see (latent-frame causality, optional local spatial window), and the
+ *      Top-K key blocks of every query block are kept                       -> lcsa_score_select
+ *   3. exact softmax attention runs over the tokens of the kept blocks only -> lcsa_attn_fwd
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are caller-owned device memory (hipMalloc / torch), the library allocates nothing.
+ *   - Token tensors are [batch, heads, tokens, head_dim] with element strides given by
+ *     lcsa_strides; the head_dim stride is 1. Tokens are in raster order n = (t*H + h)*W + w,
+ *     t counted from the tensor's first latent frame. Base pointers must be 16-byte aligned and
+ *     the batch/head/token strides multiples of 8 elements (16 bytes).
+ *   - Every device call is asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
+ *     never synchronises the host. Validation is synchronous and happens before any launch: an
+ *     invalid problem returns LCSA_ERR_INVALID / LCSA_ERR_UNSUPPORTED and launches nothing. A failed
+ *     launch returns LCSA_ERR_HIP. A device fault surfaces at the caller's next synchronisation.
+ *   - lcsa_last_error() gives a thread-local message for the last non-OK return of this thread.
+ *   - Inputs must be finite. All calls are stateless and re-entrant.
+ */
+#ifndef LCSA_H_
+#define LCSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LCSA_OK = 0,
+  LCSA_ERR_INVALID = 1,      /* inconsistent sizes, null or misaligned pointer, bad stride */
+  LCSA_ERR_UNSUPPORTED = 2,  /* a valid problem outside what the kernels implement */
+  LCSA_ERR_HIP = 3           /* a HIP runtime call or kernel launch failed */
+} lcsa_status;
+
+typedef enum { LCSA_BF16 = 0, LCSA_F32 = 1 } lcsa_dtype;
+
+/* Locality window rules (sec. 2.3 and the sec. 3 ablation name two: boundary-truncated and
+ * boundary-preserving). The window is block-granular and spatial: w_b = win/blk blocks per axis
+ * (odd), r = (w_b-1)/2. TRUNCATED keeps the blocks within r of the query block, cut at the frame
+ * edge; PRESERVING slides a w_b-wide window inward at the edge (start = clamp(c-r, 0, N-w_b)), so
+ * every query keeps w_b blocks per axis. The same window applies in every visible temporal block. */
+typedef enum { LCSA_WIN_NONE = 0, LCSA_WIN_TRUNCATED = 1, LCSA_WIN_PRESERVING = 2 } lcsa_win_mode;
+
+typedef struct {
+  int32_t batch, heads, head_dim;  /* head_dim in {64, 128} */
+  int32_t grid_h, grid_w;          /* latent tokens per frame; multiples of blk_h / blk_w */
+  int32_t kv_frames;               /* K/V hold latent frames [0, kv_frames) */
+  int32_t q_frame0, q_frames;      /* Q holds latent frames [q_frame0, q_frame0 + q_frames) */
+  int32_t blk_t, blk_h, blk_w;     /* block shape in tokens; only 2 x 8 x 8 is implemented */
+  int32_t win_mode;                /* lcsa_win_mode */
+  int32_t win_h, win_w;            /* window in tokens; win/blk must be an odd integer */
+  int32_t topk;                    /* > 0: K_i = min(topk, n_i); 0: K_i from keep_ratio */
+  double keep_ratio;               /* (0, 1]: K_i = clamp(floor(keep_ratio * n_i + 0.5), 1, n_i) */
+  float scale;                     /* softmax / block-score scale, e.g. 1/sqrt(head_dim) */
+  int32_t dtype;                   /* lcsa_dtype of Q, K, V and O */
+} lcsa_problem;
+
+typedef struct { int64_t batch, head, token; } lcsa_strides; /* in elements */
+
+/* Geometry and CSR layout of the selection (host only, pure, no device work).
+ * Query block i covers the tokens of temporal block tb_i = (q_frame0 + 2*(i / (Hb*Wb))) / blk_t,
+ * block row hb and block column wb, i = (tb_rel*Hb + hb)*Wb + wb; key block j likewise from frame 0.
+ * Key block j is visible from i iff tb_j <= tb_i (causal masking, sec. 2.2) and it lies in i's
+ * window on both axes (sec. 2.3); n_i counts them. row_ptr = exclusive prefix sum of K_i; it is the
+ * same for every (batch, head).
+ * Outputs (any may be NULL): *nqb, *nkb block counts; *nnz_per_head = row_ptr[nqb];
+ * row_ptr_host, if non-NULL, receives nqb + 1 int32 entries (call first with NULL to size it). */
+lcsa_status lcsa_csr_layout(const lcsa_problem* p, int32_t* nqb, int32_t* nkb,
+                            int32_t* nnz_per_head, int32_t* row_ptr_host);
+
+/* Block mean pooling (sec. 2.2: average pooling of Q and K over each block).
+ * q: [B, Hh, q_frames*H*W, d] (dtype), k: [B, Hh, kv_frames*H*W, d] (dtype).
+ * q_pooled: [B, Hh, nqb, d] fp32 contiguous; k_pooled: [B, Hh, nkb, d] fp32 contiguous.
+ * Each output is the mean of the block's 128 tokens, accumulated in fp64, rounded once to fp32.
+ * q (with q_pooled) or k (with k_pooled) may be NULL to pool only the other tensor. */
+lcsa_status lcsa_pool(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
+                      lcsa_strides ks, float* q_pooled, float* k_pooled, void* stream);
+
+/* Coarse block map, masks and per-row Top-K (sec. 2.2 "coarse block attention map ... Top-K block
+ * pairs"; sec. 2.3 window). For every (b, h, i): s_ij = scale * <q_pooled_i, k_pooled_j> in fp64
+ * over the visible j; keeps the K_i = row_ptr[i+1] - row_ptr[i] largest, exact ties to the lower j.
+ * row_ptr: device int32 [nqb + 1] as produced by lcsa_csr_layout.
+ * col_idx: device int32 [B, Hh, nnz_per_head]; row i's kept key blocks at
+ *          [row_ptr[i], row_ptr[i+1]) in ascending order.
+ * scores_dbg: NULL, or device fp64 [B, Hh, nqb, nkb] receiving s_ij (-inf where not visible). */
+lcsa_status lcsa_score_select(const lcsa_problem* p, const float* q_pooled, const float* k_pooled,
+                              const int32_t* row_ptr, int32_t* col_idx, double* scores_dbg,
+                              void* stream);
+
+/* Exact attention over the kept blocks (sec. 2.2 "full attention inside the selected blocks").
+ * For each query token of block i: O = softmax(scale * q K_S^T) V_S over all tokens of the blocks
+ * S = col_idx[b, h, row_ptr[i]:row_ptr[i+1]] (no token mask inside a kept block; a kept block is
+ * always fully visible under block causality and a block-granular window).
+ * q: [B, Hh, Nq, d]; k, v: [B, Hh, Nk, d]; o: [B, Hh, Nq, d], all of the problem's dtype.
+ * lse: NULL, or device fp32 [B, Hh, Nq] contiguous: natural log of the softmax denominator.
+ * Arithmetic: bf16 inputs as given (fp32 inputs are rounded to bf16 on load), bf16 MFMA with fp32
+ * accumulation for QK^T and PV, online softmax in fp32, P rounded to bf16; O written as bf16 (RNE)
+ * or fp32. col_idx entries outside [0, nkb) are skipped. */
+lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
+                          lcsa_strides ks, const void* v, lcsa_strides vs, const int32_t* row_ptr,
+                          const int32_t* col_idx, void* o, lcsa_strides os, float* lse,
+                          void* stream);
+
+const char* lcsa_status_string(lcsa_status s);
+const char* lcsa_last_error(void);   /* thread-local detail of this thread's last non-OK return */
+int32_t lcsa_version(void);          /* major*10000 + minor*100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCSA_H_ */

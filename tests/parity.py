@@ -1,0 +1,155 @@
+"""Shared parity checks: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (fixed here, used by every GPU test):
+  pooled      bf16 inputs: bit-exact with the fp64 mean rounded to fp32 (the kernel sums exactly
+              in fp64 and rounds once); fp32 inputs: within 1 fp32 ulp.
+  scores      |s_gpu - s| <= 2^-22 * scale * sum_c |qbar_c kbar_c| + 1e-12 (fp32 rounding of the
+              pooled features; the products are exact in fp64).
+  selection   per row, with s_K the oracle's K_i-th largest visible score: the kept set G must have
+              K_i entries with A <= G <= A u C, A = {s > s_K + 1e-5}, C = {|s - s_K| <= 1e-5};
+              rows with a near tie (C meets both the oracle's kept set and its complement) and rows
+              where G differs from the oracle's set are counted and reported; every other row must
+              be identical, position by position.
+  output      attention is recomputed by the oracle on the kept set the GPU chose (validated above)
+              so the error measures attention only: max |O - O_ref| <= 2e-2 and
+              mean |O - O_ref| <= 2e-3 at bf16 I/O; lse max abs <= 1e-3 for bf16 inputs, 1e-2 for
+              fp32 inputs (the kernel rounds Q/K to bf16 on load), and sum_k exp(l - lse_gpu) = 1
+              within the same bound per row (|sum - 1| is about |lse error|).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from block_sparse_causal_lcsa_amd import inputs, lcsa
+from oracle import lcsa_oracle as O
+
+NEAR_TIE = 1e-5
+O_MAX, O_MEAN = 2e-2, 2e-3
+
+
+def to_device(x: np.ndarray, device="cuda"):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(x).to(device)
+
+
+def from_device(t) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return inputs.to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.cpu().numpy().astype(np.float64)
+
+
+def run_gpu(w, x, scores=False, device="cuda"):
+    """Runs the three C-ABI calls on device copies of x; returns numpy results."""
+    p = lcsa.problem(w)
+    q, k, v = (to_device(x[n], device) for n in "qkv")
+    nqb, nkb, nnz, rp = lcsa.lcsa_csr_layout(p)
+    row_ptr = torch.from_numpy(rp).to(device)
+    qp, kp = lcsa.lcsa_pool(p, q, k)
+    dbg = torch.empty((w.batch, w.heads, nqb, nkb), dtype=torch.float64, device=device) if scores else None
+    col = lcsa.lcsa_score_select(p, qp, kp, row_ptr, scores_dbg=dbg)
+    o, lse = lcsa.lcsa_attn_fwd(p, q, k, v, row_ptr, col)
+    torch.cuda.synchronize()
+    return dict(row_ptr=rp.astype(np.int64), qbar=qp.cpu().numpy(), kbar=kp.cpu().numpy(),
+                col_idx=col.cpu().numpy().astype(np.int64), O=from_device(o), lse=lse.cpu().numpy().astype(np.float64),
+                scores=None if dbg is None else dbg.cpu().numpy())
+
+
+def check_pooled(w, gpu_bar, ref_bar):
+    ref32 = ref_bar.astype(np.float32)
+    if w.dtype == "bf16":
+        assert np.array_equal(gpu_bar, ref32), f"pooled mismatch: max |d| {np.abs(gpu_bar - ref32).max()}"
+    else:
+        ulp = np.spacing(np.abs(ref32))
+        assert np.all(np.abs(gpu_bar.astype(np.float64) - ref_bar) <= ulp), "pooled beyond 1 ulp"
+
+
+def check_scores(w, gpu_s, qbar, kbar, vis):
+    ref = O.block_scores(w, qbar, kbar, vis)
+    assert np.array_equal(np.isneginf(gpu_s), np.isneginf(ref)), "score mask differs"
+    fin = ~np.isneginf(ref)
+    bound = 2.0 ** -22 * w.scale * np.matmul(np.abs(qbar), np.swapaxes(np.abs(kbar), -1, -2)) + 1e-12
+    with np.errstate(invalid="ignore"):
+        err = np.abs(np.where(fin, gpu_s - ref, 0.0))
+    assert np.all(err <= bound), f"score error {err.max()} beyond bound"
+    return float(err.max())
+
+
+def check_selection(w, gpu, ref_scores, ref_col, row_ptr):
+    """Near-tie protocol. Returns (near_tie_rows, swapped_rows)."""
+    B, Hh, nqb, _ = ref_scores.shape
+    near, swapped = 0, 0
+    g_col, r_col = gpu["col_idx"], ref_col
+    assert np.array_equal(gpu["row_ptr"], row_ptr)
+    for b in range(B):
+        for h in range(Hh):
+            for i in range(nqb):
+                sl = slice(row_ptr[i], row_ptr[i + 1])
+                G, S = g_col[b, h, sl], r_col[b, h, sl]
+                if np.array_equal(G, S):
+                    s = ref_scores[b, h, i]
+                    k = len(S)
+                    sk = np.sort(s[np.isfinite(s)])[::-1][k - 1]
+                    C = np.flatnonzero(np.abs(s - sk) <= NEAR_TIE)
+                    if np.any(np.isin(C, S)) and np.any(~np.isin(C, S)):
+                        near += 1
+                    continue
+                s = ref_scores[b, h, i]
+                k = len(S)
+                assert np.all(np.diff(G) > 0), f"row {(b, h, i)} not strictly ascending: {G}"
+                assert np.all((G >= 0) & np.isfinite(s[np.clip(G, 0, len(s) - 1)])), f"row {(b, h, i)} invalid"
+                sk = np.sort(s[np.isfinite(s)])[::-1][k - 1]
+                A = set(np.flatnonzero(s > sk + NEAR_TIE))
+                C = set(np.flatnonzero(np.abs(s - sk) <= NEAR_TIE))
+                Gs = set(G.tolist())
+                assert A <= Gs <= (A | C), f"row {(b, h, i)}: kept set outside the near-tie band"
+                near += 1
+                swapped += 1
+    return near, swapped
+
+
+def check_attention(w, x64, gpu, qblocks=None, bh=None):
+    """Oracle attention on the GPU's kept sets for the given rows; returns error stats."""
+    q, k, v = x64
+    Oref, lref = O.attend(w, q, k, v, gpu["row_ptr"], gpu["col_idx"], qblocks=qblocks, bh=bh)
+    rows = ~np.isnan(lref)
+    Og, lg = gpu["O"], gpu["lse"]
+    dO = np.abs(Og[rows] - Oref[rows])
+    dl = np.abs(lg[rows] - lref[rows])
+    assert np.all(np.isfinite(Og[rows])) and np.all(np.isfinite(lg[rows]))
+    stats = dict(o_max=float(dO.max()), o_mean=float(dO.mean()), lse_max=float(dl.max()), rows=int(rows.sum()))
+    assert stats["o_max"] <= O_MAX, stats
+    assert stats["o_mean"] <= O_MEAN, stats
+    lse_tol = 1e-3 if w.dtype == "bf16" else 1e-2
+    assert stats["lse_max"] <= lse_tol, stats
+    # softmax normalisation with the GPU's lse, for a few rows
+    qb, kb = O.query_blocks(w), O.key_blocks(w)
+    qblocks = list(range(len(qb))) if qblocks is None else list(qblocks)
+    b, h = (0, 0) if bh is None else list(bh)[0]
+    for i in qblocks[:4]:
+        qt = O.block_tokens(w, qb[i], w.q_frame0)
+        kt = np.concatenate([O.block_tokens(w, kb[j], 0) for j in gpu["col_idx"][b, h, gpu["row_ptr"][i]:gpu["row_ptr"][i + 1]]])
+        l = w.scale * q[b, h, qt] @ k[b, h, kt].T
+        sums = np.exp(l - lg[b, h, qt][:, None]).sum(axis=1)
+        assert np.all(np.abs(sums - 1.0) <= lse_tol), sums
+    return stats
+
+
+def full_check(w, seed=0, qblocks=None, bh=None, scores=True):
+    """Runs GPU and oracle on the seeded inputs of w; checks every stage. Returns a report dict."""
+    x = inputs.make_inputs(w, seed)
+    gpu = run_gpu(w, x, scores=scores)
+    q64, k64 = inputs.to_f64(x["q"]), inputs.to_f64(x["k"])
+    vis = O.visible(w)
+    qbar, kbar = O.pool(w, q64, "q"), O.pool(w, k64, "k")
+    check_pooled(w, gpu["qbar"], qbar)
+    check_pooled(w, gpu["kbar"], kbar)
+    serr = check_scores(w, gpu["scores"], qbar, kbar, vis) if scores else None
+    s = O.block_scores(w, qbar, kbar, vis)
+    rp, col = O.select(w, s, vis)
+    near, swapped = check_selection(w, gpu, s, col, rp)
+    del s
+    stats = check_attention(w, (q64, k64, inputs.to_f64(x["v"])), gpu, qblocks=qblocks, bh=bh)
+    stats.update(near_tie_rows=near, swapped_rows=swapped, score_err=serr)
+    return stats

@@ -1,0 +1,134 @@
+"""CPU tests of the C-ABI library: it loads, exports what include/lcsa.h declares, the struct layout
+matches the header, the host geometry (lcsa_csr_layout) agrees with the oracle's independently
+written enumeration, and invalid problems are rejected before any device work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from block_sparse_causal_lcsa_amd import lcsa
+from block_sparse_causal_lcsa_amd import workloads as W
+from oracle import lcsa_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lcsa.load()
+    names = declared_functions()
+    assert set(names) == set(lcsa.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", lcsa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (lcsa_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert lib.lcsa_version() == 100
+    assert lib.lcsa_status_string(2) == b"LCSA_ERR_UNSUPPORTED"
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    fields = [f[0] for f in lcsa.LcsaProblem._fields_]
+    body = "".join(f'printf("%zu ", offsetof(lcsa_problem, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "lcsa.h"\n'
+                   f'int main(void){{ {body} printf("%zu %zu\\n", sizeof(lcsa_problem), sizeof(lcsa_strides)); return 0; }}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    want = [getattr(lcsa.LcsaProblem, f).offset for f in fields]
+    assert got[:-2] == want
+    assert got[-2:] == [ctypes.sizeof(lcsa.LcsaProblem), ctypes.sizeof(lcsa.LcsaStrides)]
+
+
+def random_problems(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hb, Wb = int(rng.integers(1, 9)), int(rng.integers(1, 12))
+        kvf = 2 * int(rng.integers(1, 5))
+        qf = 2 * int(rng.integers(1, kvf // 2 + 1))
+        q0 = 2 * int(rng.integers(0, (kvf - qf) // 2 + 1))
+        mode = int(rng.integers(0, 3))
+        wb_h, wb_w = 2 * int(rng.integers(0, 5)) + 1, 2 * int(rng.integers(0, 5)) + 1
+        topk = int(rng.integers(0, 6))
+        rho = float(rng.choice([0.05, 0.136, 0.25, 1 / 3, 0.5, 0.77, 1.0]))
+        out.append(W.Workload("r", 1, 2, 64, 8 * Hb, 8 * Wb, kvf, q0, qf, win_mode=mode,
+                              win_h=8 * wb_h if mode else 0, win_w=8 * wb_w if mode else 0,
+                              topk=topk, keep_ratio=rho))
+    return out
+
+
+@pytest.mark.parametrize("w", W.ALL + random_problems(40, 0), ids=lambda w: w.name)
+def test_csr_layout_matches_oracle(w):
+    nqb, nkb, nnz, rp = lcsa.lcsa_csr_layout(lcsa.problem(w))
+    ref = O.csr_row_ptr(w)
+    assert (nqb, nkb) == (w.nqb, w.nkb)
+    assert nnz == ref[-1]
+    assert np.array_equal(rp.astype(np.int64), ref)
+
+
+BASE = W.CHUNK_768
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(head_dim=96), lcsa.LCSA_ERR_UNSUPPORTED),
+    (dict(head_dim=0), lcsa.LCSA_ERR_UNSUPPORTED),
+    (dict(grid_w=84), lcsa.LCSA_ERR_UNSUPPORTED),
+    (dict(blk_h=4), lcsa.LCSA_ERR_UNSUPPORTED),
+    (dict(q_frame0=3, q_frames=2), lcsa.LCSA_ERR_UNSUPPORTED),
+    (dict(kv_frames=7), lcsa.LCSA_ERR_UNSUPPORTED),
+    (dict(q_frame0=6), lcsa.LCSA_ERR_INVALID),
+    (dict(batch=0), lcsa.LCSA_ERR_INVALID),
+    (dict(topk=-1), lcsa.LCSA_ERR_INVALID),
+    (dict(keep_ratio=0.0), lcsa.LCSA_ERR_INVALID),
+    (dict(keep_ratio=1.5), lcsa.LCSA_ERR_INVALID),
+    (dict(keep_ratio=float("nan")), lcsa.LCSA_ERR_INVALID),
+    (dict(win_mode=1, win_h=64, win_w=72), lcsa.LCSA_ERR_INVALID),
+    (dict(win_mode=2, win_h=0, win_w=72), lcsa.LCSA_ERR_INVALID),
+    (dict(win_mode=5, win_h=72, win_w=72), lcsa.LCSA_ERR_INVALID),
+])
+def test_invalid_problems_rejected_on_host(change, status):
+    w = BASE.replace(**change)
+    p = lcsa.problem(w)
+    lib = lcsa.load()
+    assert lib.lcsa_csr_layout(ctypes.byref(p), None, None, None, None) == status
+    assert lib.lcsa_last_error()
+    # the device entry points validate first and return before touching HIP
+    zs = lcsa.LcsaStrides(0, 0, 0)
+    assert lib.lcsa_pool(ctypes.byref(p), None, zs, None, zs, None, None, None) == status
+    assert lib.lcsa_score_select(ctypes.byref(p), None, None, None, None, None, None) == status
+    assert lib.lcsa_attn_fwd(ctypes.byref(p), None, zs, None, zs, None, zs, None, None, None, zs, None, None) == status
+
+
+def test_bad_pointers_and_strides_rejected_on_host():
+    lib = lcsa.load()
+    p = lcsa.problem(BASE)
+    d = BASE.head_dim
+    good = lcsa.LcsaStrides(12 * 25344 * d, 25344 * d, d)
+    buf = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    zs = lcsa.LcsaStrides(0, 0, 0)
+    assert lib.lcsa_pool(ctypes.byref(p), None, zs, None, zs, None, None, None) == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_pool(ctypes.byref(p), None, zs, mis, good, None, buf, None) == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_pool(ctypes.byref(p), None, zs, buf, lcsa.LcsaStrides(0, 0, d - 8), None, buf, None) \
+        == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_pool(ctypes.byref(p), None, zs, buf, lcsa.LcsaStrides(0, 0, d + 4), None, buf, None) \
+        == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_pool(ctypes.byref(p), None, zs, buf, good, None, None, None) == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_score_select(ctypes.byref(p), buf, buf, None, buf, None, None) == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_attn_fwd(ctypes.byref(p), buf, good, buf, good, buf, good, buf, buf, mis, good, None, None) \
+        == lcsa.LCSA_ERR_INVALID
+    assert b"aligned" in lib.lcsa_last_error()
+    big = BASE.replace(kv_frames=40, q_frame0=38)            # 1320 key blocks > one LDS row
+    pb = lcsa.problem(big)
+    assert lib.lcsa_score_select(ctypes.byref(pb), buf, buf, buf, buf, None, None) == lcsa.LCSA_ERR_UNSUPPORTED

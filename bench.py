@@ -1,0 +1,205 @@
+"""LCSA forward benchmark on one MI355X.
+
+One step = one LCSA forward over one streaming chunk: lcsa_pool -> lcsa_score_select ->
+lcsa_attn_fwd through the C ABI, inputs resident in HBM. Default workload: one 768x1408 streaming
+chunk (2 query latent frames over 6, 12 heads, d = 128, bf16, 13.6% of blocks kept).
+
+Prints one JSON line. `value` is the effective TFLOP/s on the selected blocks over the whole step
+(sum over kept (head, i, j) pairs of 4*128*128*d FLOP / step time); `ms_per_step` is the time per
+8-frame chunk. `roofline` is for the dominant kernel (lcsa_attn_fwd) against the dense bf16 MFMA
+peak; its duration is measured with HIP events on the launch stream. `cpu_baseline` times the fp64
+oracle on the host cores on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_causal_lcsa_amd", "csrc", "attn_fwd.hip")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per attn_fwd launch from the committed rocprofv3 counter summary, or None when
+    the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_hash():
+        return None
+    return float(t.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="chunk_768x1408_q2_kv6")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=0,
+                    help="query blocks per head in the oracle sample (0 = all)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the LCSA forward here runs on a single MI355X; "
+              "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_sparse_causal_lcsa_amd import inputs, lcsa
+    from block_sparse_causal_lcsa_amd import workloads as W
+
+    w = W.BY_NAME[args.workload]
+    p = lcsa.problem(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = inputs.make_inputs(w, seed=0)
+
+    def dev_t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = dev_t(x["q"]), dev_t(x["k"]), dev_t(x["v"])
+    nqb, nkb, nnz, rp = lcsa.lcsa_csr_layout(p)
+    row_ptr = torch.from_numpy(rp).to(dev)
+    qp = torch.empty((w.batch, w.heads, nqb, w.head_dim), dtype=torch.float32, device=dev)
+    kp = torch.empty((w.batch, w.heads, nkb, w.head_dim), dtype=torch.float32, device=dev)
+    col = torch.empty((w.batch, w.heads, nnz), dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads, w.nq_tokens), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    pairs = w.batch * w.heads * nnz
+    flop = pairs * 4.0 * 128 * 128 * w.head_dim
+    esz = 2 if w.dtype == "bf16" else 4
+    pool_bytes = w.batch * w.heads * ((w.nq_tokens + w.nk_tokens) * w.head_dim * esz + (nqb + nkb) * w.head_dim * 4)
+    sel_bytes = w.batch * w.heads * ((nqb + nkb) * w.head_dim * 4 + nnz * 4)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        lcsa.lcsa_pool(p, q, k, qp, kp, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        lcsa.lcsa_score_select(p, qp, kp, row_ptr, col, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        lcsa.lcsa_attn_fwd(p, q, k, v, row_ptr, col, o, lse, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing: K back-to-back steps between two synchronisations
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-kernel durations with HIP events on the launch stream (a second timed pass)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    t_pool = [e[0].elapsed_time(e[1]) for e in evs]
+    t_sel = [e[1].elapsed_time(e[2]) for e in evs]
+    t_attn = [e[2].elapsed_time(e[3]) for e in evs]
+    t_step_ev = [e[0].elapsed_time(e[3]) for e in evs]
+    med = lambda a: float(np.median(a))
+    attn_ms = float(np.mean(t_attn))
+    achieved = flop / (attn_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(w.name)
+
+    out = {
+        "metric": "LCSA fwd effective TFLOP/s on selected blocks + ms per 8-frame chunk",
+        "value": round(flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded smooth sinusoidal Q/K fields + 0.5 N(0,1), V ~ N(0,1)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "grid": [w.grid_h, w.grid_w], "q_frames": [w.q_frame0, w.q_frame0 + w.q_frames],
+                   "kv_frames": w.kv_frames, "keep_ratio": w.keep_ratio if not w.topk else None,
+                   "topk": w.topk or None, "window": ["none", "truncated", "preserving"][w.win_mode],
+                   "selected_pairs": pairs, "selected_gflop": round(flop / 1e9, 2)},
+        "ms_per_chunk": round(ms_per_step, 4),
+        "kernels_ms_median": {"lcsa_pool": round(med(t_pool), 4), "lcsa_score_select": round(med(t_sel), 4),
+                              "lcsa_attn_fwd": round(med(t_attn), 4), "step_events": round(med(t_step_ev), 4)},
+        "pool_gbs": round(pool_bytes / (med(t_pool) * 1e-3) / 1e9, 1),
+        "score_select_gbs": round(sel_bytes / (med(t_sel) * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "kernel": "lcsa_attn_fwd", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "flop_per_launch": flop, "avg_launch_ms": round(attn_ms, 4)},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_sample_blocks)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, x, sample_blocks):
+    """The fp64 oracle, unchanged, on this host: pool + score + select over the whole chunk and
+    exact attention over a sample of query blocks (every head), scaled to TFLOP/s on the selected
+    blocks it computed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from block_sparse_causal_lcsa_amd import inputs
+    from oracle import lcsa_oracle as O
+
+    q64, k64, v64 = (inputs.to_f64(x[n]) for n in "qkv")
+    nqb = w.nqb
+    qblocks = list(range(nqb)) if sample_blocks <= 0 else list(np.linspace(0, nqb - 1, sample_blocks).astype(int))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        vis = O.visible(w)
+        qbar, kbar = O.pool(w, q64, "q"), O.pool(w, k64, "k")
+        s = O.block_scores(w, qbar, kbar, vis)
+        rp, col = O.select(w, s, vis)
+        O.attend(w, q64, k64, v64, rp, col, qblocks=qblocks)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    kept = sum(int(rp[i + 1] - rp[i]) for i in qblocks) * w.batch * w.heads
+    flop = kept * 4.0 * 128 * 128 * w.head_dim
+    blas = [t for t in threadpool_info() if t.get("user_api") == "blas"]
+    cores = max([t.get("num_threads", 1) for t in blas] or [1])
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"median of 3 runs; {w.name}: pool+score+select of all {nqb} query blocks, attention of "
+                      f"{len(qblocks)} query blocks x {w.batch * w.heads} heads ({kept} kept pairs); "
+                      f"numpy fp64, BLAS threads={cores}, elementwise single-threaded"}
+
+
+if __name__ == "__main__":
+    main()

@@ -49,8 +49,15 @@ constexpr int kPadK = 8;  // bf16 elements of padding per LDS row
 
 // Token index (within its tensor) of row r (0..127) of block (tr, hb, wb), tr relative to the
 // tensor's first temporal block.
-__device__ __forceinline__ int64_t block_token(const Geom& g, int tr, int hb, int wb, int r) {
-  return (int64_t(kBlkT * tr + (r >> 6)) * g.H + kBlkH * hb + ((r >> 3) & 7)) * g.W + kBlkW * wb + (r & 7);
+__device__ __forceinline__ int block_token(const Geom& g, int tr, int hb, int wb, int r) {
+  return ((kBlkT * tr + (r >> 6)) * g.H + kBlkH * hb + ((r >> 3) & 7)) * g.W + kBlkW * wb + (r & 7);
+}
+
+// Loads through a uniform (per-workgroup) base pointer plus a 32-bit byte offset, so each address
+// costs one VGPR. The host guarantees every per-(batch, head) tensor span is below 4 GiB.
+template <typename V>
+__device__ __forceinline__ V load_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const V*>(static_cast<const char*>(base) + byte_off);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -69,41 +76,54 @@ struct Stage {
   uint32_t v[VIT][8];
 };
 
+// Token offset, relative to the block's first token, of key row r (0..127) of a block.
+__device__ __forceinline__ int rel_token(const Geom& g, int r) {
+  return (r >> 6) * g.H * g.W + ((r >> 3) & 7) * g.W + (r & 7);
+}
+
+// Loads key block j into the staging registers. Every address is
+//   (uniform block base) + (wave-uniform row offset) + (loop-invariant per-lane offset),
+// so only the last part lives in a VGPR and the rest is scalar arithmetic.
 template <typename T, int D>
-__device__ __forceinline__ void stage_load(Stage<T, D>& st, const T* kb, const T* vb, int64_t kst, int64_t vst,
-                                           const Geom& g, int j) {
+__device__ __forceinline__ void stage_load(Stage<T, D>& st, const T* kb, const T* vb, uint32_t kst, uint32_t vst,
+                                           const Geom& g, int j, uint32_t k_lane_off, uint32_t v_lane_off) {
+  constexpr uint32_t ES = sizeof(T);
+  constexpr int CPR = D / 8;        // 8-element chunks per key row
+  constexpr int RPI = 256 / CPR;    // key rows per workgroup-wide iteration
   const int tr = j / g.bpt, rem = j - (j / g.bpt) * g.bpt;
   const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
-  const int t = threadIdx.x;
-  constexpr int CPR = D / 8;  // 8-element chunks per key row
+  const uint32_t base_tok = uint32_t((kBlkT * tr * g.H + kBlkH * hb) * g.W + kBlkW * wb);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* kbase = reinterpret_cast<const char*>(kb) + base_tok * kst * ES;
+  const char* vbase = reinterpret_cast<const char*>(vb) + base_tok * vst * ES;
 #pragma unroll
   for (int it = 0; it < Stage<T, D>::KCH; ++it) {
-    const int id = t + 256 * it;
-    const int r = id / CPR, c = id % CPR;
-    const T* src = kb + block_token(g, tr, hb, wb, r) * kst + 8 * c;
-    if constexpr (sizeof(T) == 2) {
-      const uint4 x = *reinterpret_cast<const uint4*>(src);
+    // rows RPI*it + (RPI/4)*wave + lane/CPR: the lane part stays inside one 8-token row
+    const uint32_t soff = uint32_t(rel_token(g, RPI * it + (RPI / 4) * wave)) * kst * ES;
+    if constexpr (ES == 2) {
+      const uint4 x = load_at<uint4>(kbase + soff, k_lane_off);
       st.k[it][0] = x.x; st.k[it][1] = x.y; st.k[it][2] = x.z; st.k[it][3] = x.w;
     } else {
-      const float4 x0 = *reinterpret_cast<const float4*>(src);
-      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      const float4 x0 = load_at<float4>(kbase + soff, k_lane_off);
+      const float4 x1 = load_at<float4>(kbase + soff, k_lane_off + 16);
       st.k[it][0] = pack_bf16x2(x0.x, x0.y); st.k[it][1] = pack_bf16x2(x0.z, x0.w);
       st.k[it][2] = pack_bf16x2(x1.x, x1.y); st.k[it][3] = pack_bf16x2(x1.z, x1.w);
     }
   }
-  const int wave = t >> 6, lane = t & 63;
-  const int dl = lane % (D / 2);        // d pair index
-  const int grp = lane / (D / 2);       // which of the VGRP key groups this lane serves
 #pragma unroll
   for (int u = 0; u < Stage<T, D>::VIT; ++u) {
-    const int r0 = 8 * ((wave * Stage<T, D>::VIT + u) * Stage<T, D>::VGRP + grp);
+    // unit U = (wave*VIT + u)*VGRP + grp covers V^T columns 8U..8U+7 = keys
+    // 16*(U/2) + 4*(U%2) + {0..3, 8..11}; U/2 is wave-uniform, U%2 (only when VGRP = 2) is in the lane offset
+    const int G = ((wave * Stage<T, D>::VIT + u) * Stage<T, D>::VGRP) >> 1;
+    const int hsel = Stage<T, D>::VGRP == 1 ? (u & 1) : 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const T* src = vb + block_token(g, tr, hb, wb, r0 + e) * vst + 2 * dl;
-      if constexpr (sizeof(T) == 2) {
-        st.v[u][e] = *reinterpret_cast<const uint32_t*>(src);
+      const int r = 16 * G + 4 * hsel + (e >> 2) * 8 + (e & 3);
+      const uint32_t soff = uint32_t(rel_token(g, r)) * vst * ES;
+      if constexpr (ES == 2) {
+        st.v[u][e] = load_at<uint32_t>(vbase + soff, v_lane_off);
       } else {
-        const float2 x = *reinterpret_cast<const float2*>(src);
+        const float2 x = load_at<float2>(vbase + soff, v_lane_off);
         st.v[u][e] = pack_bf16x2(x.x, x.y);
       }
     }
@@ -126,7 +146,7 @@ __device__ __forceinline__ void stage_store(const Stage<T, D>& st, uint16_t* Ks,
   const int grp = lane / (D / 2);
 #pragma unroll
   for (int u = 0; u < Stage<T, D>::VIT; ++u) {
-    const int r0 = 8 * ((wave * Stage<T, D>::VIT + u) * Stage<T, D>::VGRP + grp);
+    const int r0 = 8 * ((wave * Stage<T, D>::VIT + u) * Stage<T, D>::VGRP + grp);  // V^T column
     const uint32_t* w = st.v[u];
     // low halves -> row d = 2*dl, high halves -> row 2*dl + 1; 8 consecutive keys each
     const uint4 lo = make_uint4(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u),
@@ -139,7 +159,7 @@ __device__ __forceinline__ void stage_store(const Stage<T, D>& st, uint16_t* Ks,
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int KP = D + kPadK, VP = kBN + kPadK;
   constexpr int DS = D / 16;  // 16-wide d steps of the QK^T MFMA
   constexpr int DT = D / 32;  // 32-wide d tiles of the output
@@ -162,12 +182,12 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 
   const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
   const int qhb = qrem / g.Wb, qwb = qrem - (qrem / g.Wb) * g.Wb;
-  const int64_t qtok = block_token(g, qtr, qhb, qwb, 32 * wave + l32);
+  const int qtok = block_token(g, qtr, qhb, qwb, 32 * wave + l32);
 
   // B operand of S^T = K Q^T: lane holds Q[row l32][16*s + 8*hi + 0..7]
   bf16x8 qf[DS];
   {
-    const T* src = qb + qtok * a.qst + 8 * hi;
+    const T* src = qb + int64_t(qtok) * a.qst + 8 * hi;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       if constexpr (sizeof(T) == 2) {
@@ -181,6 +201,10 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
     }
   }
 
+  const uint32_t kst32 = static_cast<uint32_t>(a.kst), vst32 = static_cast<uint32_t>(a.vst);
+  // per-lane parts of the staging addresses (see stage_load)
+  const uint32_t k_lane_off = ((lane / (D / 8)) * kst32 + 8 * (lane % (D / 8))) * uint32_t(sizeof(T));
+  const uint32_t v_lane_off = (4 * (lane / (D / 2)) * vst32 + 2 * (lane % (D / 2))) * uint32_t(sizeof(T));
   const int beg = a.row_ptr[i], nsel = a.row_ptr[i + 1] - beg;
   const int32_t* sel = a.col_idx + int64_t(bh) * a.nnz + beg;
 
@@ -192,29 +216,32 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   Stage<T, D> st;
   int jn = nsel > 0 ? sel[0] : 0;
   bool ok_next = jn >= 0 && jn < g.nkb;
-  if (nsel > 0) stage_load<T, D>(st, kb, vb, a.kst, a.vst, g, ok_next ? jn : 0);
+  if (nsel > 0) stage_load<T, D>(st, kb, vb, kst32, vst32, g, ok_next ? jn : 0, k_lane_off, v_lane_off);
 
   for (int n = 0; n < nsel; ++n) {
     const bool ok = ok_next;
     __syncthreads();  // every wave is done reading the previous block
     stage_store<T, D>(st, Ks, Vt);
     __syncthreads();
-    if (n + 1 < nsel) {
+    const bool more = n + 1 < nsel;
+    if (more) {
       jn = sel[n + 1];
       ok_next = jn >= 0 && jn < g.nkb;
-      stage_load<T, D>(st, kb, vb, a.kst, a.vst, g, ok_next ? jn : 0);
     }
-    if (!ok) continue;
+    if (!ok) {
+      if (more) stage_load<T, D>(st, kb, vb, kst32, vst32, g, ok_next ? jn : 0, k_lane_off, v_lane_off);
+      continue;
+    }
 
-    // S^T tiles: 4 x (32 keys x 32 queries)
+    // S^T tiles: 4 x (32 keys x 32 queries); the four accumulators are independent chains
     f32x16 sacc[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      sacc[kt] = f32x16{};
-      const uint16_t* kr = Ks + (kt * 32 + l32) * KP + 8 * hi;
+    for (int kt = 0; kt < 4; ++kt) sacc[kt] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
+    for (int s = 0; s < DS; ++s) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + l32) * KP + 8 * hi + 16 * s);
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
       }
     }
@@ -249,26 +276,25 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
 
+    // the next block's loads overlap the PV MFMAs (issued here to keep fewer registers live)
+    if (more) stage_load<T, D>(st, kb, vb, kst32, vst32, g, ok_next ? jn : 0, k_lane_off, v_lane_off);
+
     // O^T += V^T P^T. MFMA k-slot 8*hi + e of step (kt, h2) is key kt*32 + 16*h2 + 8*(e/4) + 4*hi + e%4,
-    // which is where the score layout put P; V^T is read in the same order (two 4-key runs).
+    // where the score layout put P; V^T stores those 8 keys contiguously (columns 16*(2kt+h2) + 8*hi).
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vr = Vt + (dt * 32 + l32) * VP + 4 * hi;
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vr + kt * 32 + 16 * h2);
-          const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vr + kt * 32 + 16 * h2 + 8);
-          const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vt + (dt * 32 + l32) * VP + 16 * (2 * kt + h2) + 8 * hi);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kt][h2], oacc[dt], 0, 0, 0);
         }
-    }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  T* ob = static_cast<T*>(a.o) + b * a.osb + h * a.osh + block_token(g, qtr, qhb, qwb, 32 * wave + l32) * a.ost;
+  T* ob = static_cast<T*>(a.o) + b * a.osb + h * a.osh + int64_t(qtok) * a.ost;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -285,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
     }
   if (a.lse && hi == 0) {
     const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-    a.lse[int64_t(bh) * a.nq_tok + block_token(g, qtr, qhb, qwb, 32 * wave + l32)] = lse;
+    a.lse[int64_t(bh) * a.nq_tok + qtok] = lse;
   }
 }
 
@@ -311,6 +337,10 @@ extern "C" lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_
     return fail(LCSA_ERR_INVALID, "lcsa_attn_fwd: misaligned row_ptr, col_idx or lse");
   int32_t nnz = 0;
   if ((st = lcsa_csr_layout(p, nullptr, nullptr, &nnz, nullptr)) != LCSA_OK) return st;
+  const int64_t esz = dtype_size(p);
+  if ((hw * p->kv_frames * ks.token + p->head_dim) * esz >= (int64_t(1) << 32) ||
+      (hw * p->kv_frames * vs.token + p->head_dim) * esz >= (int64_t(1) << 32))
+    return fail(LCSA_ERR_UNSUPPORTED, "lcsa_attn_fwd: a per-head K or V span exceeds 4 GiB");
   AttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.row_ptr = row_ptr; a.col_idx = col_idx;
   a.qsb = qs.batch; a.qsh = qs.head; a.qst = qs.token;

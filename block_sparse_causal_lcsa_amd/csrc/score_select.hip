@@ -2,12 +2,12 @@
 // (FlashVSR summary, sec. 2.2: a coarse block-to-block attention map from the pooled features,
 // the Top-K most relevant block pairs are kept; sec. 2.3: the local spatial window).
 //
-// One workgroup (4 waves) per (batch, head, tile of 16 query blocks).
+// One workgroup (16 waves) per (batch, head, tile of 16 query blocks).
 //  1. Scores: s_ij = scale * <qbar_i, kbar_j> for the tile's 16 rows against every key block up to
 //     the last temporal block the tile can see, as fp64 MFMA 16x16x4 tiles (the pooled fp32
 //     features are widened exactly). Column tiles with no visible entry are skipped. Rows of 16
 //     fp64 scores live in LDS, -inf where the key block is not visible.
-//  2. Selection, one wave per row: scores map to order-preserving 64-bit keys; a most-significant-
+//  2. Selection, one wave per row (all 16 rows in parallel): scores map to order-preserving 64-bit keys; a most-significant-
 //     bit-first radix select over the wave's candidates (ballot + popcount per bit) finds the key of
 //     the K_i-th largest score and how many of the keys equal to it are still needed; equal keys are
 //     taken lowest index first. Kept indices are emitted in ascending order with ballot prefix sums.
@@ -23,7 +23,8 @@ namespace {
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRows = 16;                 // query blocks per workgroup
+constexpr int kRows = 16;                 // query blocks per workgroup, one wave each
+constexpr int kThreads = 64 * kRows;
 constexpr int kMaxCols = 1248;            // key blocks one row can hold in LDS
 constexpr int kMaxSlots = (kMaxCols + 63) / 64;
 constexpr int kLdsPad = 2;
@@ -52,7 +53,7 @@ __device__ __forceinline__ uint64_t order_key(double s) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void score_select_kernel(SelArgs a) {
+__global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
   extern __shared__ double S[];  // [kRows][a.ld]
   const Geom& g = a.g;
   const int tiles = (g.nqb + kRows - 1) / kRows;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelArgs a) {
     tbi[rr] = qblock_window(g, rv[rr] ? i : r0, &h0[rr], &h1[rr], &w0[rr], &w1[rr]);
   }
 
-  for (int ct = wave; ct < nct; ct += 4) {
+  for (int ct = wave; ct < nct; ct += kRows) {
     const int j = ct * 16 + lr;
     bool vis[4];
     bool any = false;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelArgs a) {
 
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
   const int nslots = (ncol + 63) / 64;
-  for (int rl = wave; rl < rows; rl += 4) {
+  for (int rl = wave; rl < rows; rl += kRows) {
     const int i = r0 + rl;
     const double* srow = S + rl * a.ld;
     if (a.dbg) {
@@ -217,13 +218,13 @@ extern "C" lcsa_status lcsa_score_select(const lcsa_problem* p, const float* q_p
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)),
                          "lcsa_score_select LDS size")) != LCSA_OK)
       return st;
-    score_select_kernel<128><<<wgs, 256, lds, s>>>(a);
+    score_select_kernel<128><<<wgs, kThreads, lds, s>>>(a);
   } else {
     if ((st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<64>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)),
                          "lcsa_score_select LDS size")) != LCSA_OK)
       return st;
-    score_select_kernel<64><<<wgs, 256, lds, s>>>(a);
+    score_select_kernel<64><<<wgs, kThreads, lds, s>>>(a);
   }
   return hip_status(hipGetLastError(), "lcsa_score_select launch");
 }

@@ -41,8 +41,13 @@ struct AttnArgs {
   int32_t nnz;
   int32_t nq_tok;       // query tokens per (batch, head)
   int32_t nwg;
-  float c;              // scale * log2(e)
+  float c;              // scale * log2(e), > 0
+  uint32_t k_span, v_span;  // bytes of one (batch, head) slice of K / V
 };
+
+// The running row maximum is only raised when a block's maximum exceeds it by more than this
+// (log2 units): P then stays below 2^kLazyMax and O is rescaled only on those rare blocks.
+constexpr float kLazyMax = 8.0f;
 
 constexpr int kBN = 128;  // keys per kept block
 constexpr int kPadK = 8;  // bf16 elements of padding per LDS row
@@ -53,11 +58,15 @@ __device__ __forceinline__ int block_token(const Geom& g, int tr, int hb, int wb
   return ((kBlkT * tr + (r >> 6)) * g.H + kBlkH * hb + ((r >> 3) & 7)) * g.W + kBlkW * wb + (r & 7);
 }
 
-// Loads through a uniform (per-workgroup) base pointer plus a 32-bit byte offset, so each address
-// costs one VGPR. The host guarantees every per-(batch, head) tensor span is below 4 GiB.
-template <typename V>
-__device__ __forceinline__ V load_at(const void* base, uint32_t byte_off) {
-  return *reinterpret_cast<const V*>(static_cast<const char*>(base) + byte_off);
+// Raw buffer resource over one (batch, head) slice of a token tensor: loads take a 32-bit lane
+// offset (VGPR) plus a 32-bit uniform offset (SGPR), so gathers cost no vector ALU work, and any
+// access past `bytes` returns zero instead of touching memory. The host guarantees spans < 4 GiB.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBufDword3 = 0x00020000;  // raw 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufDword3);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -82,11 +91,11 @@ __device__ __forceinline__ int rel_token(const Geom& g, int r) {
 }
 
 // Loads key block j into the staging registers. Every address is
-//   (uniform block base) + (wave-uniform row offset) + (loop-invariant per-lane offset),
-// so only the last part lives in a VGPR and the rest is scalar arithmetic.
+//   (uniform block base + wave-uniform row offset) [SGPR] + (loop-invariant per-lane offset) [VGPR].
 template <typename T, int D>
-__device__ __forceinline__ void stage_load(Stage<T, D>& st, const T* kb, const T* vb, uint32_t kst, uint32_t vst,
-                                           const Geom& g, int j, uint32_t k_lane_off, uint32_t v_lane_off) {
+__device__ __forceinline__ void stage_load(Stage<T, D>& st, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                           uint32_t kst, uint32_t vst, const Geom& g, int j,
+                                           uint32_t k_lane_off, uint32_t v_lane_off) {
   constexpr uint32_t ES = sizeof(T);
   constexpr int CPR = D / 8;        // 8-element chunks per key row
   constexpr int RPI = 256 / CPR;    // key rows per workgroup-wide iteration
@@ -94,20 +103,20 @@ __device__ __forceinline__ void stage_load(Stage<T, D>& st, const T* kb, const T
   const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
   const uint32_t base_tok = uint32_t((kBlkT * tr * g.H + kBlkH * hb) * g.W + kBlkW * wb);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const char* kbase = reinterpret_cast<const char*>(kb) + base_tok * kst * ES;
-  const char* vbase = reinterpret_cast<const char*>(vb) + base_tok * vst * ES;
 #pragma unroll
   for (int it = 0; it < Stage<T, D>::KCH; ++it) {
     // rows RPI*it + (RPI/4)*wave + lane/CPR: the lane part stays inside one 8-token row
-    const uint32_t soff = uint32_t(rel_token(g, RPI * it + (RPI / 4) * wave)) * kst * ES;
+    const uint32_t soff = (base_tok + uint32_t(rel_token(g, RPI * it + (RPI / 4) * wave))) * kst * ES;
     if constexpr (ES == 2) {
-      const uint4 x = load_at<uint4>(kbase + soff, k_lane_off);
-      st.k[it][0] = x.x; st.k[it][1] = x.y; st.k[it][2] = x.z; st.k[it][3] = x.w;
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(kr, k_lane_off, soff, 0);
+      st.k[it][0] = x[0]; st.k[it][1] = x[1]; st.k[it][2] = x[2]; st.k[it][3] = x[3];
     } else {
-      const float4 x0 = load_at<float4>(kbase + soff, k_lane_off);
-      const float4 x1 = load_at<float4>(kbase + soff, k_lane_off + 16);
-      st.k[it][0] = pack_bf16x2(x0.x, x0.y); st.k[it][1] = pack_bf16x2(x0.z, x0.w);
-      st.k[it][2] = pack_bf16x2(x1.x, x1.y); st.k[it][3] = pack_bf16x2(x1.z, x1.w);
+      const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(kr, k_lane_off, soff, 0);
+      const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(kr, k_lane_off + 16, soff, 0);
+      st.k[it][0] = pack_bf16x2(__uint_as_float(x0[0]), __uint_as_float(x0[1]));
+      st.k[it][1] = pack_bf16x2(__uint_as_float(x0[2]), __uint_as_float(x0[3]));
+      st.k[it][2] = pack_bf16x2(__uint_as_float(x1[0]), __uint_as_float(x1[1]));
+      st.k[it][3] = pack_bf16x2(__uint_as_float(x1[2]), __uint_as_float(x1[3]));
     }
   }
 #pragma unroll
@@ -119,12 +128,12 @@ __device__ __forceinline__ void stage_load(Stage<T, D>& st, const T* kb, const T
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int r = 16 * G + 4 * hsel + (e >> 2) * 8 + (e & 3);
-      const uint32_t soff = uint32_t(rel_token(g, r)) * vst * ES;
+      const uint32_t soff = (base_tok + uint32_t(rel_token(g, r))) * vst * ES;
       if constexpr (ES == 2) {
-        st.v[u][e] = load_at<uint32_t>(vbase + soff, v_lane_off);
+        st.v[u][e] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_lane_off, soff, 0);
       } else {
-        const float2 x = load_at<float2>(vbase + soff, v_lane_off);
-        st.v[u][e] = pack_bf16x2(x.x, x.y);
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(vr, v_lane_off, soff, 0);
+        st.v[u][e] = pack_bf16x2(__uint_as_float(x[0]), __uint_as_float(x[1]));
       }
     }
   }
@@ -202,6 +211,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 
   const uint32_t kst32 = static_cast<uint32_t>(a.kst), vst32 = static_cast<uint32_t>(a.vst);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, a.k_span), vrs = make_rsrc(vb, a.v_span);
   // per-lane parts of the staging addresses (see stage_load)
   const uint32_t k_lane_off = ((lane / (D / 8)) * kst32 + 8 * (lane % (D / 8))) * uint32_t(sizeof(T));
   const uint32_t v_lane_off = (4 * (lane / (D / 2)) * vst32 + 2 * (lane % (D / 2))) * uint32_t(sizeof(T));
@@ -214,24 +224,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   Stage<T, D> st;
+  // entries outside [0, nkb) are replaced by block 0 and contribute exactly zero (see neg_m)
   int jn = nsel > 0 ? sel[0] : 0;
   bool ok_next = jn >= 0 && jn < g.nkb;
-  if (nsel > 0) stage_load<T, D>(st, kb, vb, kst32, vst32, g, ok_next ? jn : 0, k_lane_off, v_lane_off);
+  stage_load<T, D>(st, krs, vrs, kst32, vst32, g, ok_next ? jn : 0, k_lane_off, v_lane_off);
 
   for (int n = 0; n < nsel; ++n) {
     const bool ok = ok_next;
+    const int jcur = ok ? jn : 0;
     __syncthreads();  // every wave is done reading the previous block
     stage_store<T, D>(st, Ks, Vt);
     __syncthreads();
-    const bool more = n + 1 < nsel;
-    if (more) {
-      jn = sel[n + 1];
-      ok_next = jn >= 0 && jn < g.nkb;
-    }
-    if (!ok) {
-      if (more) stage_load<T, D>(st, kb, vb, kst32, vst32, g, ok_next ? jn : 0, k_lane_off, v_lane_off);
-      continue;
-    }
+    // next block (the last iteration re-reads the current one, which is in L2, to keep the loop
+    // free of branches around the staging registers)
+    jn = n + 1 < nsel ? sel[n + 1] : jcur;
+    ok_next = jn >= 0 && jn < g.nkb;
 
     // S^T tiles: 4 x (32 keys x 32 queries); the four accumulators are independent chains
     f32x16 sacc[4];
@@ -245,19 +252,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
       }
     }
-    // online softmax in the log2 domain; this lane holds 64 of the row's 128 scores
+    // online softmax in the log2 domain; this lane holds 64 of the row's 128 raw scores
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sacc[kt][v] *= a.c;
-        mx = fmaxf(mx, sacc[kt][v]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
+    mx = ok ? fmaxf(mx, __shfl_xor(mx, 32)) * a.c : -INFINITY;  // c > 0, so max(c s) = c max(s)
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyMax)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+    }
+    const float neg_m = ok ? -m_run : -INFINITY;  // a skipped entry gives P = exp2(-inf) = 0
     float ls = 0.f;
     bf16x8 pf[4][2];
 #pragma unroll
@@ -266,18 +278,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[kt][8 * h2 + e] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * h2 + e], a.c, neg_m));
           ls += pv;
           pf[kt][h2][e] = (__bf16)pv;
         }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+    l_run += ls;
 
     // the next block's loads overlap the PV MFMAs (issued here to keep fewer registers live)
-    if (more) stage_load<T, D>(st, kb, vb, kst32, vst32, g, ok_next ? jn : 0, k_lane_off, v_lane_off);
+    stage_load<T, D>(st, krs, vrs, kst32, vst32, g, ok_next ? jn : 0, k_lane_off, v_lane_off);
 
     // O^T += V^T P^T. MFMA k-slot 8*hi + e of step (kt, h2) is key kt*32 + 16*h2 + 8*(e/4) + 4*hi + e%4,
     // where the score layout put P; V^T stores those 8 keys contiguously (columns 16*(2kt+h2) + 8*hi).
@@ -353,6 +361,8 @@ extern "C" lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_
   a.nq_tok = static_cast<int32_t>(hw * p->q_frames);
   a.nwg = p->batch * p->heads * g.nqb;
   a.c = static_cast<float>(static_cast<double>(p->scale) * 1.4426950408889634);
+  a.k_span = static_cast<uint32_t>((hw * p->kv_frames - 1) * ks.token * esz + p->head_dim * esz);
+  a.v_span = static_cast<uint32_t>((hw * p->kv_frames - 1) * vs.token * esz + p->head_dim * esz);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (p->dtype == LCSA_BF16) {

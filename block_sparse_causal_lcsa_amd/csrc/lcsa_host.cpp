@@ -63,7 +63,8 @@ lcsa_status validate_problem(const lcsa_problem* p, Geom* g) {
   if (p->topk < 0) return fail(LCSA_ERR_INVALID, "topk %d < 0", p->topk);
   if (p->topk == 0 && !(p->keep_ratio > 0.0 && p->keep_ratio <= 1.0))
     return fail(LCSA_ERR_INVALID, "keep_ratio must be in (0, 1] when topk == 0");
-  if (!std::isfinite(p->scale)) return fail(LCSA_ERR_INVALID, "scale is not finite");
+  if (!std::isfinite(p->scale) || !(p->scale > 0.0f))
+    return fail(LCSA_ERR_INVALID, "scale must be finite and positive");
 
   const int64_t hw = static_cast<int64_t>(p->grid_h) * p->grid_w;
   const int64_t nk_tok = hw * p->kv_frames;

@@ -61,7 +61,7 @@ typedef struct {
   int32_t win_h, win_w;            /* window in tokens; win/blk must be an odd integer */
   int32_t topk;                    /* > 0: K_i = min(topk, n_i); 0: K_i from keep_ratio */
   double keep_ratio;               /* (0, 1]: K_i = clamp(floor(keep_ratio * n_i + 0.5), 1, n_i) */
-  float scale;                     /* softmax / block-score scale, e.g. 1/sqrt(head_dim) */
+  float scale;                     /* softmax / block-score scale (> 0), e.g. 1/sqrt(head_dim) */
   int32_t dtype;                   /* lcsa_dtype of Q, K, V and O */
 } lcsa_problem;
 

@@ -98,8 +98,18 @@ BASE = W.CHUNK_768
     (dict(win_mode=5, win_h=72, win_w=72), lcsa.LCSA_ERR_INVALID),
 ])
 def test_invalid_problems_rejected_on_host(change, status):
-    w = BASE.replace(**change)
-    p = lcsa.problem(w)
+    _check_rejected(BASE.replace(**change), status)
+
+
+def test_nonpositive_scale_rejected_on_host():
+    for scale in (0.0, -0.088, float("inf")):
+        p = lcsa.problem(BASE)
+        p.scale = scale
+        _check_rejected(p, lcsa.LCSA_ERR_INVALID)
+
+
+def _check_rejected(w_or_p, status):
+    p = w_or_p if isinstance(w_or_p, lcsa.LcsaProblem) else lcsa.problem(w_or_p)
     lib = lcsa.load()
     assert lib.lcsa_csr_layout(ctypes.byref(p), None, None, None, None) == status
     assert lib.lcsa_last_error()

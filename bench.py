@@ -56,6 +56,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=0,
                     help="query blocks per head in the oracle sample (0 = all)")
+    ap.add_argument("--profile", action="store_true",
+                    help="for rocprofv3 counter runs: warmup + `steps` steps, then one plain device copy "
+                         "of 256 MiB (the byte-counter calibration kernel); prints a short line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the LCSA forward here runs on a single MI355X; "
@@ -111,6 +114,18 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    if args.profile:
+        for _ in range(args.steps):
+            step()
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"profile run: {args.steps} steps of {w.name}; calibration copy 268435456 bytes", flush=True)
+        return
 
     # whole-step timing: K back-to-back steps between two synchronisations
     t0 = time.perf_counter()

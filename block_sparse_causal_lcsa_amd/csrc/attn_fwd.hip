@@ -26,6 +26,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
   const void* q;
@@ -323,6 +324,223 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------------------------------------------
+// bf16 inputs: each kept key block is processed as two 64-key sub-blocks (its two latent frames).
+// Sub-block tiles of K and V go straight from memory into LDS with buffer loads (no registers, no
+// LDS stores), double-buffered, so one workgroup barrier per sub-block both publishes the tile that
+// just landed and frees the buffer the next loads go to.
+//   K tile: [key][d], 16-byte chunk c of key row r at chunk position c ^ (r mod CPR): the QK^T
+//           fragment reads (16 lanes on 16 consecutive rows, one chunk) hit distinct banks.
+//   V tile: [key][d], chunk c of row r at c ^ vswz(r); the PV operand (V^T) is read with
+//           ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of the 8-byte
+//           pieces addressed by lanes 4k + (i%16)/4, k = 0..3, so pointing lane j at key row
+//           K0 + j/4, columns d0 + 4(j%4) delivers V[K0 + k][d0 + i%16] to lane i: four consecutive
+//           keys of one head-dim column, exactly an MFMA A-operand half.
+constexpr int kSub = 64;  // keys per sub-block
+
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;               // 16-byte chunks per key row
+  static constexpr int LOADS = kSub * CPR / 256;  // 16-byte loads per lane per tile
+  static constexpr int ELEMS = kSub * D;          // bf16 elements per tile
+};
+
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return Tile<D>::CPR >= 16 ? 4 * (r & 3) : 4 * (r & 1);
+}
+
+// Issues the loads of one sub-block tile (K or V) of `ELEMS` bf16 into LDS at `tile`.
+// Rows r of the tile are tokens (r/8)*W + r%8 after `base_tok` (one latent frame of the block).
+template <int D, bool IS_V>
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* tile, uint32_t tst, uint32_t base_tok,
+                                           int W, int wave, int lane) {
+  constexpr int CPR = Tile<D>::CPR;
+#pragma unroll
+  for (int it = 0; it < Tile<D>::LOADS; ++it) {
+    const int slot0 = (wave * Tile<D>::LOADS + it) * 64;  // first 16-byte slot of this wave instruction
+    const int r0 = slot0 / CPR;                           // first row (a multiple of 64 / CPR)
+    const int r = r0 + lane / CPR;                        // stays inside one 8-token row
+    const int pos = lane % CPR;
+    const int c = pos ^ (IS_V ? vswz<D>(r) : (r & (CPR - 1)));
+    const uint32_t soff = (base_tok + uint32_t((r0 / 8) * W + (r0 % 8))) * tst * 2u;
+    const uint32_t voff = (uint32_t(lane / CPR) * tst + 8u * uint32_t(c)) * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(tile + slot0 * 8), 16, voff, soff, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_fwd_direct_kernel(AttnArgs a) {
+  constexpr int DS = D / 16;  // 16-wide d steps of the QK^T MFMA
+  constexpr int DT = D / 32;  // 32-wide d tiles of the output
+  constexpr int CPR = Tile<D>::CPR;
+  constexpr int TE = Tile<D>::ELEMS;
+  // two buffers, each [K | V]; separate arrays so the compiler can tell the buffer being read from
+  // the one the in-flight loads write
+  __shared__ __attribute__((aligned(16))) uint16_t buf0[2 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t buf1[2 * TE];
+
+  const Geom& g = a.g;
+  int wg = blockIdx.x;
+  const int n8 = (a.nwg / 8) * 8;
+  if (wg < n8) wg = (wg % 8) * (a.nwg / 8) + wg / 8;
+  const int bh = wg / g.nqb, i = wg - (wg / g.nqb) * g.nqb;
+  const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
+
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + b * a.qsb + h * a.qsh;
+  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + b * a.ksb + h * a.ksh;
+  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + b * a.vsb + h * a.vsh;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
+  const int qhb = qrem / g.Wb, qwb = qrem - (qrem / g.Wb) * g.Wb;
+  const int qtok = block_token(g, qtr, qhb, qwb, 32 * wave + l32);
+
+  // B operand of S^T = K Q^T: lane holds Q[row l32][16*s + 8*hi + 0..7]
+  bf16x8 qf[DS];
+  {
+    const uint16_t* src = qb + int64_t(qtok) * a.qst + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
+  }
+
+  const uint32_t kst = static_cast<uint32_t>(a.kst), vst = static_cast<uint32_t>(a.vst);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, a.k_span), vrs = make_rsrc(vb, a.v_span);
+  const int beg = a.row_ptr[i], nsel = a.row_ptr[i + 1] - beg;
+  const int32_t* sel = a.col_idx + int64_t(bh) * a.nnz + beg;
+  const int total = 2 * nsel;
+  const uint32_t hw = uint32_t(g.H) * uint32_t(g.W);
+
+  // first token of sub-block m (block sel[m/2], latent frame m%2); entries outside [0, nkb) use
+  // block 0 and are masked out of the softmax
+  auto sub_base = [&](int m, bool& ok) -> uint32_t {
+    int j = sel[m >> 1];
+    ok = j >= 0 && j < g.nkb;
+    j = ok ? j : 0;
+    const int tr = j / g.bpt, rem = j - (j / g.bpt) * g.bpt;
+    const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
+    return uint32_t((kBlkT * tr * g.H + kBlkH * hb) * g.W + kBlkW * wb) + uint32_t(m & 1) * hw;
+  };
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // lane parts of the LDS fragment addresses
+  const int kx = l32 & (CPR - 1);  // K swizzle of rows kt*32 + l32
+  const int jj = lane & 15;
+  const int vrow = 4 * hi + jj / 4;                 // V^T read: row offset inside a 16-key group
+  const int vcol = (lane & 16) + 4 * (jj & 3);      // and column offset inside a 32-wide d tile
+
+  bool ok_next = true;
+  uint32_t base_next = total > 0 ? sub_base(0, ok_next) : 0;
+  if (total > 0) {
+    issue_tile<D, false>(krs, buf0, kst, base_next, g.W, wave, lane);
+    issue_tile<D, true>(vrs, buf0 + TE, vst, base_next, g.W, wave, lane);
+  }
+
+  // one sub-block: wait for its tile in `cur`, start loading the next one into `nxt`, compute
+  auto step = [&](int m, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
+    const bool ok = ok_next;
+    const uint16_t* Kt = cur;
+    const uint16_t* Vt = cur + TE;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this lane's tile loads have landed
+    __syncthreads();  // every lane's have; and every wave is done with the other buffer
+    if (m + 1 < total) {
+      base_next = sub_base(m + 1, ok_next);
+      uint16_t* nk = nxt;
+      issue_tile<D, false>(krs, nk, kst, base_next, g.W, wave, lane);
+      issue_tile<D, true>(vrs, nk + TE, vst, base_next, g.W, wave, lane);
+    }
+
+    // S^T: 2 x (32 keys x 32 queries)
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kt + (kt * 32 + l32) * D + (((2 * s + hi) ^ kx) * 8));
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
+    mx = ok ? fmaxf(mx, __shfl_xor(mx, 32)) * a.c : -INFINITY;  // c > 0
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyMax)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+    }
+    const float neg_m = ok ? -m_run : -INFINITY;
+    float ls = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * h2 + e], a.c, neg_m));
+          ls += pv;
+          pf[kt][h2][e] = (__bf16)pv;
+        }
+    l_run += ls;
+
+    // O^T += V^T P^T; k-slot 8*hi + e of step (kt, h2) is key kt*32 + 16*h2 + 8*(e/4) + 4*hi + e%4
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          v4i16 part[2];
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const int row = kt * 32 + 16 * h2 + 8 * e2 + vrow;
+            const int col = dt * 32 + vcol;
+            const uint16_t* p = Vt + row * D + ((((col >> 3) ^ vswz<D>(row)) << 3) | (col & 7));
+            part[e2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+          }
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kt][h2], oacc[dt], 0, 0, 0);
+        }
+  };
+  for (int m = 0; m < total; m += 2) {
+    step(m, buf0, buf1);
+    if (m + 1 < total) step(m + 1, buf1, buf0);
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  uint16_t* ob = static_cast<uint16_t*>(a.o) + b * a.osb + h * a.osh + int64_t(qtok) * a.ost;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = dt * 32 + 8 * g4 + 4 * hi;
+      *reinterpret_cast<uint2*>(ob + d0) =
+          make_uint2(pack_bf16x2(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv),
+                     pack_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv));
+    }
+  if (a.lse && hi == 0) {
+    const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    a.lse[int64_t(bh) * a.nq_tok + qtok] = lse;
+  }
+}
+
 }  // namespace
 }  // namespace lcsa
 
@@ -366,8 +584,8 @@ extern "C" lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (p->dtype == LCSA_BF16) {
-    if (p->head_dim == 128) attn_fwd_kernel<uint16_t, 128><<<a.nwg, 256, 0, s>>>(a);
-    else attn_fwd_kernel<uint16_t, 64><<<a.nwg, 256, 0, s>>>(a);
+    if (p->head_dim == 128) attn_fwd_direct_kernel<128><<<a.nwg, 256, 0, s>>>(a);
+    else attn_fwd_direct_kernel<64><<<a.nwg, 256, 0, s>>>(a);
   } else {
     if (p->head_dim == 128) attn_fwd_kernel<float, 128><<<a.nwg, 256, 0, s>>>(a);
     else attn_fwd_kernel<float, 64><<<a.nwg, 256, 0, s>>>(a);

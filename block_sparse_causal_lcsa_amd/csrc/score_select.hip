@@ -52,7 +52,7 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-template <int D>
+template <int D, int SLOTS>
 __global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
   extern __shared__ double S[];  // [kRows][a.ld]
   const Geom& g = a.g;
@@ -99,14 +99,17 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
     if (__any(any)) {
       const float* krow = kmat + int64_t(min(j, ncol - 1)) * D;
+      // four independent accumulation chains (channel e of each float4), summed in a fixed order
+      f64x4 c[4] = {acc, acc, acc, acc};
 #pragma unroll
       for (int m = 0; m < D / 16; ++m) {
         const float4 kb = *reinterpret_cast<const float4*>(krow + 16 * m + 4 * lg);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].x, (double)kb.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].y, (double)kb.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].z, (double)kb.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].w, (double)kb.w, acc, 0, 0, 0);
+        c[0] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].x, (double)kb.x, c[0], 0, 0, 0);
+        c[1] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].y, (double)kb.y, c[1], 0, 0, 0);
+        c[2] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].z, (double)kb.z, c[2], 0, 0, 0);
+        c[3] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].w, (double)kb.w, c[3], 0, 0, 0);
       }
+      acc = (c[0] + c[1]) + (c[2] + c[3]);
     }
     // result item rr of lane (lr, lg) is D[row lg + 4*rr][col lr]
 #pragma unroll
@@ -115,7 +118,6 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
   __syncthreads();
 
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
-  const int nslots = (ncol + 63) / 64;
   for (int rl = wave; rl < rows; rl += kRows) {
     const int i = r0 + rl;
     const double* srow = S + rl * a.ld;
@@ -126,22 +128,17 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
     const int K = a.row_ptr[i + 1] - a.row_ptr[i];
     int32_t* out = a.col_idx + int64_t(bh) * a.nnz + a.row_ptr[i];
 
-    uint64_t key[kMaxSlots];
-    uint32_t cand = 0;
+    // non-candidates (masked, beyond the row) get key 0, below every candidate's key; the loops
+    // below are branch-free over a fixed slot count
+    uint64_t key[SLOTS];
     int ncand = 0;
 #pragma unroll
-    for (int m = 0; m < kMaxSlots; ++m) {
-      key[m] = 0;
-      if (m < nslots) {
-        const int j = lane + 64 * m;
-        const double s = j < ncol ? srow[j] : -INFINITY;
-        const bool c = s != -INFINITY;
-        if (c) {
-          key[m] = order_key(s);
-          cand |= 1u << m;
-        }
-        ncand += __popcll(__ballot(c));
-      }
+    for (int m = 0; m < SLOTS; ++m) {
+      const int j = lane + 64 * m;
+      const double s = j < ncol ? srow[j] : -INFINITY;
+      const bool c = s != -INFINITY;
+      key[m] = c ? order_key(s) : 0;
+      ncand += __popcll(__ballot(c));
     }
     int need = min(K, ncand);
     uint64_t prefix = 0, mask = 0;
@@ -150,12 +147,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
       const uint64_t bm = uint64_t(1) << bit;
       int cnt1 = 0;
 #pragma unroll
-      for (int m = 0; m < kMaxSlots; ++m) {
-        if (m < nslots) {
-          const bool e = ((cand >> m) & 1u) && (key[m] & mask) == prefix && (key[m] & bm);
-          cnt1 += __popcll(__ballot(e));
-        }
-      }
+      for (int m = 0; m < SLOTS; ++m) cnt1 += __popcll(__ballot(((key[m] & mask) == prefix) & ((key[m] & bm) != 0)));
       if (cnt1 >= need) {
         prefix |= bm;
         eq = cnt1;
@@ -165,24 +157,33 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
       }
       mask |= bm;
     }
-    // kept: masked key above the prefix, or equal to it and among the first `need` such (by j)
+    // kept: masked key above the prefix, or equal to it and among the first `need` such (by j);
+    // key 0 is never kept (a kept key is at least the K-th largest candidate key, which is > 0)
     int written = 0, ties = 0;
 #pragma unroll
-    for (int m = 0; m < kMaxSlots; ++m) {
-      if (m < nslots) {
-        const bool c = (cand >> m) & 1u;
-        const uint64_t km = key[m] & mask;
-        const bool tie = c && km == prefix;
-        const uint64_t tb = __ballot(tie);
-        const bool sel = (c && km > prefix) || (tie && ties + __popcll(tb & lt_mask) < need);
-        ties += __popcll(tb);
-        const uint64_t sb = __ballot(sel);
-        if (sel) out[written + __popcll(sb & lt_mask)] = lane + 64 * m;
-        written += __popcll(sb);
-      }
+    for (int m = 0; m < SLOTS; ++m) {
+      const uint64_t km = key[m] & mask;
+      const bool c = key[m] != 0;
+      const bool tie = c & (km == prefix);
+      const uint64_t tb = __ballot(tie);
+      const bool sel = (c & (km > prefix)) | (tie & (ties + __popcll(tb & lt_mask) < need));
+      ties += __popcll(tb);
+      const uint64_t sb = __ballot(sel);
+      if (sel) out[written + __popcll(sb & lt_mask)] = lane + 64 * m;
+      written += __popcll(sb);
     }
     for (int s = written + lane; s < K; s += 64) out[s] = -1;  // only if row_ptr asks for > n_i
   }
+}
+
+template <int D, int SLOTS>
+lcsa_status launch(const SelArgs& a, int wgs, size_t lds, hipStream_t s) {
+  lcsa_status st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<D, SLOTS>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)),
+                              "lcsa_score_select LDS size");
+  if (st != LCSA_OK) return st;
+  score_select_kernel<D, SLOTS><<<wgs, kThreads, lds, s>>>(a);
+  return LCSA_OK;
 }
 
 }  // namespace
@@ -213,18 +214,18 @@ extern "C" lcsa_status lcsa_score_select(const lcsa_problem* p, const float* q_p
   const int wgs = p->batch * p->heads * ((g.nqb + kRows - 1) / kRows);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  const int slots = (g.nkb + 63) / 64;
   if (p->head_dim == 128) {
-    if ((st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<128>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)),
-                         "lcsa_score_select LDS size")) != LCSA_OK)
-      return st;
-    score_select_kernel<128><<<wgs, kThreads, lds, s>>>(a);
+    if (slots <= 4) st = launch<128, 4>(a, wgs, lds, s);
+    else if (slots <= 8) st = launch<128, 8>(a, wgs, lds, s);
+    else if (slots <= 16) st = launch<128, 16>(a, wgs, lds, s);
+    else st = launch<128, kMaxSlots>(a, wgs, lds, s);
   } else {
-    if ((st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<64>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)),
-                         "lcsa_score_select LDS size")) != LCSA_OK)
-      return st;
-    score_select_kernel<64><<<wgs, kThreads, lds, s>>>(a);
+    if (slots <= 4) st = launch<64, 4>(a, wgs, lds, s);
+    else if (slots <= 8) st = launch<64, 8>(a, wgs, lds, s);
+    else if (slots <= 16) st = launch<64, 16>(a, wgs, lds, s);
+    else st = launch<64, kMaxSlots>(a, wgs, lds, s);
   }
+  if (st != LCSA_OK) return st;
   return hip_status(hipGetLastError(), "lcsa_score_select launch");
 }

@@ -1,22 +1,25 @@
 // lcsa_attn_fwd: exact softmax attention of each 128-token query block over the tokens of its kept
 // key blocks (FlashVSR summary, sec. 2.2: full attention is applied inside the selected blocks only).
 //
-// One workgroup (4 waves, 256 lanes) per (batch, head, query block); wave w owns query rows
-// 32w..32w+31 of the block. For every kept key block j (128 tokens):
-//   - K_j is staged in LDS row-major [key][d] and V_j transposed [d][key] (bf16), from registers that
-//     were loaded from HBM/L2 while the previous block was being computed;
-//   - S^T = K_j Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the wave's Q rows held in
-//     registers). In the result each lane holds one query row (lane % 32) and half of the key
-//     columns, so the online softmax needs one cross-lane max per block and no other exchange;
-//   - the scores become P = exp2(S * scale * log2(e) - m) in fp32 (running max m, running sum l),
-//     P is rounded to bf16 and used directly as the B operand of O^T += V_j^T P^T: the k-order of
-//     the PV MFMA is permuted to match the score layout, and V^T is read from LDS in that order.
-// At the end O = O / l (bf16 RNE or fp32) and lse = ln(sum exp(scale q.k)) in fp32.
+// Shared by both kernels below: a wave owns 32 query rows. Scores are computed transposed,
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = key rows from LDS, B = the wave's Q rows held in
+// registers), so each lane holds one query row (lane % 32) and half of the 64 or 128 key columns
+// and the online softmax needs no cross-lane traffic beyond one swap of row halves. P = exp2(S *
+// scale * log2(e) - m) in fp32 is rounded to bf16 and is directly the B operand of O^T += V^T P^T:
+// the k-order of the P V MFMA is permuted to match the score layout, and V^T is read from LDS in
+// that order. At the end O = O / l (bf16 RNE or fp32) and lse = ln(sum exp(scale q.k)) in fp32.
 // Workgroup ids are remapped so that consecutive query blocks of one head run on the same XCD,
 // whose L2 then serves the key blocks that neighbouring query blocks share.
+//
+//  - bf16 (attn_fwd_pp_kernel): 8 waves per workgroup, two query blocks, K/V tiles loaded
+//    directly into LDS, matrix and vector phases of the two blocks interleaved ("ping-pong").
+//  - fp32 inputs (attn_fwd_kernel): 4 waves per workgroup and query block; tiles are staged through
+//    registers, where fp32 is rounded to bf16.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "lcsa_internal.h"
 
@@ -44,6 +47,8 @@ struct AttnArgs {
   int32_t nwg;
   float c;              // scale * log2(e), > 0
   uint32_t k_span, v_span;  // bytes of one (batch, head) slice of K / V
+  FastDiv div_bpt, div_wb;  // division by g.bpt and g.Wb
+  int32_t nrows;            // (batch, head, query block) rows = B * Hh * nqb
 };
 
 // The running row maximum is only raised when a block's maximum exceeds it by more than this
@@ -328,8 +333,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 // ------------------------------------------------------------------------------------------------
 // bf16 inputs: each kept key block is processed as two 64-key sub-blocks (its two latent frames).
 // Sub-block tiles of K and V go straight from memory into LDS with buffer loads (no registers, no
-// LDS stores), double-buffered, so one workgroup barrier per sub-block both publishes the tile that
-// just landed and frees the buffer the next loads go to.
+// LDS stores).
 //   K tile: [key][d], 16-byte chunk c of key row r at chunk position c ^ (r mod CPR): the QK^T
 //           fragment reads (16 lanes on 16 consecutive rows, one chunk) hit distinct banks.
 //   V tile: [key][d], chunk c of row r at c ^ vswz(r); the PV operand (V^T) is read with
@@ -338,6 +342,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 //           K0 + j/4, columns d0 + 4(j%4) delivers V[K0 + k][d0 + i%16] to lane i: four consecutive
 //           keys of one head-dim column, exactly an MFMA A-operand half.
 constexpr int kSub = 64;  // keys per sub-block
+// Bound on a lane's sum of 32 unnormalised probabilities before the running maximum is refreshed:
+// every P stays below 2^16, far from overflowing the fp32 accumulators for finite inputs.
+constexpr float kSumMax = 65536.0f;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct Tile {
@@ -353,176 +361,302 @@ __device__ __forceinline__ int vswz(int r) {
 
 // Issues the loads of one sub-block tile (K or V) of `ELEMS` bf16 into LDS at `tile`.
 // Rows r of the tile are tokens (r/8)*W + r%8 after `base_tok` (one latent frame of the block).
+// Load `it` (0 .. LOADS-1) of this wave's share of a tile: 64 lanes x 16 bytes.
+template <int D, bool IS_V>
+__device__ __forceinline__ void issue_tile_part(__amdgpu_buffer_rsrc_t rs, uint16_t* tile, uint32_t tst, uint32_t base_tok,
+                                                int W, int wave, int lane, int it) {
+  constexpr int CPR = Tile<D>::CPR;
+  const int slot0 = (wave * Tile<D>::LOADS + it) * 64;  // first 16-byte slot of this wave instruction
+  const int r0 = slot0 / CPR;                           // first row (a multiple of 64 / CPR)
+  const int r = r0 + lane / CPR;                        // stays inside one 8-token row
+  const int pos = lane % CPR;
+  const int c = pos ^ (IS_V ? vswz<D>(r) : (r & (CPR - 1)));
+  const uint32_t soff = (base_tok + uint32_t((r0 / 8) * W + (r0 % 8))) * tst * 2u;
+  const uint32_t voff = (uint32_t(lane / CPR) * tst + 8u * uint32_t(c)) * 2u;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)(tile + slot0 * 8), 16, voff, soff, 0, 0);
+}
+
 template <int D, bool IS_V>
 __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* tile, uint32_t tst, uint32_t base_tok,
                                            int W, int wave, int lane) {
-  constexpr int CPR = Tile<D>::CPR;
 #pragma unroll
-  for (int it = 0; it < Tile<D>::LOADS; ++it) {
-    const int slot0 = (wave * Tile<D>::LOADS + it) * 64;  // first 16-byte slot of this wave instruction
-    const int r0 = slot0 / CPR;                           // first row (a multiple of 64 / CPR)
-    const int r = r0 + lane / CPR;                        // stays inside one 8-token row
-    const int pos = lane % CPR;
-    const int c = pos ^ (IS_V ? vswz<D>(r) : (r & (CPR - 1)));
-    const uint32_t soff = (base_tok + uint32_t((r0 / 8) * W + (r0 % 8))) * tst * 2u;
-    const uint32_t voff = (uint32_t(lane / CPR) * tst + 8u * uint32_t(c)) * 2u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(tile + slot0 * 8), 16, voff, soff, 0, 0);
+  for (int it = 0; it < Tile<D>::LOADS; ++it) issue_tile_part<D, IS_V>(rs, tile, tst, base_tok, W, wave, lane, it);
+}
+
+// Largest raw score of this lane's query row over the tile (both lane halves hold halves of a row).
+__device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[2]) {
+  float m0 = s[0][0], m1 = s[1][0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) {
+    m0 = fmaxf(m0, s[0][v]);
+    m1 = fmaxf(m1, s[1][v]);
+  }
+  const float mx = fmaxf(m0, m1);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// ------------------------------------------------------------------------------------------------
+// Ping-pong schedule (bf16). A workgroup of 8 waves owns two query blocks: waves 0-3 (group 0) the
+// first, waves 4-7 (group 1) the second; wave w and wave w+4 share a SIMD. Time is cut into phases
+// that end at workgroup barriers. In every phase one group runs its matrix phase (P V of the
+// previous sub-block and Q K^T of the current one: 32 MFMAs per wave) while the other runs its
+// vector phase (row max, exponentials, row sums of the current sub-block), and the roles swap at
+// the next barrier, so each SIMD always has one wave feeding the matrix core and one on the vector
+// ALU. Group 1 starts one phase late.
+// Per group, M(m) reads K(m) and V(m-1) from LDS; the vector phase V(m) issues the direct-to-LDS
+// loads of K(m+2) and V(m+1) (their buffers were last read in M(m)) and, at its end, waits for the
+// loads of K(m+1) and V(m), issued one vector phase earlier, which M(m+1) reads.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+// Barrier between phases without a memory fence: the direct-to-LDS loads in flight stay in flight.
+// Every LDS read this wave issued has completed (lgkmcnt(0)).
+// Nothing is scheduled across it, so every phase keeps its own instructions.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Waits until at most n (0, 1 or 2) tiles' worth of this lane's direct-to-LDS loads are in flight.
+template <int LOADS>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if (n >= 2) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
+  } else if (n == 1) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_direct_kernel(AttnArgs a) {
-  constexpr int DS = D / 16;  // 16-wide d steps of the QK^T MFMA
-  constexpr int DT = D / 32;  // 32-wide d tiles of the output
+__device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int row_start, int nsel, int nsel_other, int lwave,
+                                         uint16_t* kb0, uint16_t* kb1, uint16_t* vb0, uint16_t* vb1) {
+  constexpr int DS = D / 16;
+  constexpr int DT = D / 32;
   constexpr int CPR = Tile<D>::CPR;
-  constexpr int TE = Tile<D>::ELEMS;
-  // two buffers, each [K | V]; separate arrays so the compiler can tell the buffer being read from
-  // the one the in-flight loads write
-  __shared__ __attribute__((aligned(16))) uint16_t buf0[2 * TE];
-  __shared__ __attribute__((aligned(16))) uint16_t buf1[2 * TE];
-
+  constexpr int LOADS = Tile<D>::LOADS;
   const Geom& g = a.g;
-  int wg = blockIdx.x;
-  const int n8 = (a.nwg / 8) * 8;
-  if (wg < n8) wg = (wg % 8) * (a.nwg / 8) + wg / 8;
-  const int bh = wg / g.nqb, i = wg - (wg / g.nqb) * g.nqb;
-  const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
-
-  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + b * a.qsb + h * a.qsh;
-  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + b * a.ksb + h * a.ksh;
-  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + b * a.vsb + h * a.vsh;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
+  const int t = 2 * nsel;
+  const int t_other = 2 * nsel_other;
+  const int phases = 2 * (t > t_other ? t : t_other) + 2;  // common phase count of both groups
+  int phase = 0;
 
+  const bool has = qblk >= 0;
+  const int bh = has ? qblk / g.nqb : 0, i = has ? qblk - bh * g.nqb : 0;
+  const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + b * a.qsb + h * a.qsh;
+  const uint16_t* kbp = static_cast<const uint16_t*>(a.k) + b * a.ksb + h * a.ksh;
+  const uint16_t* vbp = static_cast<const uint16_t*>(a.v) + b * a.vsb + h * a.vsh;
   const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
   const int qhb = qrem / g.Wb, qwb = qrem - (qrem / g.Wb) * g.Wb;
-  const int qtok = block_token(g, qtr, qhb, qwb, 32 * wave + l32);
+  const int qtok = block_token(g, qtr, qhb, qwb, 32 * lwave + l32);
 
-  // B operand of S^T = K Q^T: lane holds Q[row l32][16*s + 8*hi + 0..7]
   bf16x8 qf[DS];
-  {
+  if (has) {
     const uint16_t* src = qb + int64_t(qtok) * a.qst + 8 * hi;
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
   }
 
   const uint32_t kst = static_cast<uint32_t>(a.kst), vst = static_cast<uint32_t>(a.vst);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, a.k_span), vrs = make_rsrc(vb, a.v_span);
-  const int beg = a.row_ptr[i], nsel = a.row_ptr[i + 1] - beg;
-  const int32_t* sel = a.col_idx + int64_t(bh) * a.nnz + beg;
-  const int total = 2 * nsel;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbp, a.k_span), vrs = make_rsrc(vbp, a.v_span);
+  // the column list is read-only for the whole launch: read it through the scalar cache (uniform
+  // scalar loads, which leave the vector-memory counter to the tile loads)
+  const const_i32* sel = (const const_i32*)(a.col_idx) + int64_t(bh) * a.nnz + (has ? row_start : 0);
   const uint32_t hw = uint32_t(g.H) * uint32_t(g.W);
-
-  // first token of sub-block m (block sel[m/2], latent frame m%2); entries outside [0, nkb) use
-  // block 0 and are masked out of the softmax
-  auto sub_base = [&](int m, bool& ok) -> uint32_t {
-    int j = sel[m >> 1];
+  auto block_base = [&](int j, bool& ok) -> uint32_t {
     ok = j >= 0 && j < g.nkb;
-    j = ok ? j : 0;
-    const int tr = j / g.bpt, rem = j - (j / g.bpt) * g.bpt;
-    const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
-    return uint32_t((kBlkT * tr * g.H + kBlkH * hb) * g.W + kBlkW * wb) + uint32_t(m & 1) * hw;
+    const uint32_t ju = ok ? uint32_t(j) : 0u;
+    const uint32_t tr = fast_div(ju, a.div_bpt), rem = ju - tr * uint32_t(g.bpt);
+    const uint32_t hb = fast_div(rem, a.div_wb), wb = rem - hb * uint32_t(g.Wb);
+    return (kBlkT * tr * uint32_t(g.H) + kBlkH * hb) * uint32_t(g.W) + kBlkW * wb;
   };
 
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-
-  // lane parts of the LDS fragment addresses
-  const int kx = l32 & (CPR - 1);  // K swizzle of rows kt*32 + l32
+  const int kx = l32 & (CPR - 1);
   const int jj = lane & 15;
-  const int vrow = 4 * hi + jj / 4;                 // V^T read: row offset inside a 16-key group
-  const int vcol = (lane & 16) + 4 * (jj & 3);      // and column offset inside a 32-wide d tile
+  const int vrow = 4 * hi + jj / 4;
+  const int vcol = (lane & 16) + 4 * (jj & 3);
 
-  bool ok_next = true;
-  uint32_t base_next = total > 0 ? sub_base(0, ok_next) : 0;
-  if (total > 0) {
-    issue_tile<D, false>(krs, buf0, kst, base_next, g.W, wave, lane);
-    issue_tile<D, true>(vrs, buf0 + TE, vst, base_next, g.W, wave, lane);
+  // block n = current (ok_c, base_c), n + 1 (ok_n, base_n), entry of n + 2 (j_pref)
+  bool ok_c = false, ok_n = false;
+  uint32_t base_c = 0, base_n = 0;
+  int j_pref = 0;
+  if (t > 0) {
+    base_c = block_base(sel[0], ok_c);
+    if (nsel > 1) base_n = block_base(sel[1], ok_n);
+    if (nsel > 2) j_pref = sel[2];
+    issue_tile<D, false>(krs, kb0, kst, base_c, g.W, lwave, lane);
+    issue_tile<D, false>(krs, kb1, kst, base_c + hw, g.W, lwave, lane);
+    issue_tile<D, true>(vrs, vb0, vst, base_c, g.W, lwave, lane);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  phase_barrier();
+  if (G == 1) {
+    phase_barrier();
+    ++phase;
   }
 
-  // one sub-block: wait for its tile in `cur`, start loading the next one into `nxt`, compute
-  auto step = [&](int m, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
-    const bool ok = ok_next;
-    const uint16_t* Kt = cur;
-    const uint16_t* Vt = cur + TE;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this lane's tile loads have landed
-    __syncthreads();  // every lane's have; and every wave is done with the other buffer
-    if (m + 1 < total) {
-      base_next = sub_base(m + 1, ok_next);
-      uint16_t* nk = nxt;
-      issue_tile<D, false>(krs, nk, kst, base_next, g.W, wave, lane);
-      issue_tile<D, true>(vrs, nk + TE, vst, base_next, g.W, wave, lane);
-    }
+  f32x16 S[2];
+  bf16x8 pf[2][2];
 
-    // S^T: 2 x (32 keys x 32 queries)
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // matrix phase: O += V^T P^T of the previous sub-block (tile Vp), S = K Q^T of the current (tile Kc).
+  // Every MFMA takes one 16-byte operand fragment
+  // from LDS, read kLook MFMAs ahead so the LDS latency hides behind the matrix core.
+  auto mphase = [&](const uint16_t* Vp, const uint16_t* Kc, auto pv_tag, auto qk_tag) __attribute__((always_inline)) {
+    constexpr bool do_pv = decltype(pv_tag)::value, do_qk = decltype(qk_tag)::value;
+    constexpr int NQ = do_qk ? 2 * DS : 0;  // Q K^T MFMAs: (d step st, key tile kt)
+    constexpr int NP = do_pv ? 4 * DT : 0;  // P V MFMAs: (key tile kt, half h2, d tile dt)
+    constexpr int NOPS = NQ + NP;
+    constexpr int kLook = 4;
+    // op j: with both products, even j are Q K^T ops and odd j are P V ops
+    auto is_qk = [](int j) { return NP == 0 ? true : (NQ == 0 ? false : (j % 2 == 0)); };
+    auto sub = [](int j) { return (NP == 0 || NQ == 0) ? j : j / 2; };
+    auto load = [&](int j) -> bf16x8 {
+      if (is_qk(j)) {
+        const int q = sub(j), st = q >> 1, kt = q & 1;
+        return *reinterpret_cast<const bf16x8*>(Kc + (kt * 32 + l32) * D + (((2 * st + hi) ^ kx) * 8));
+      }
+      const int q = sub(j), kt = q / (2 * DT), h2 = (q / DT) & 1, dt = q % DT;
+      v4i16 part[2];
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int row = kt * 32 + 16 * h2 + 8 * e2 + vrow;
+        const int col = dt * 32 + vcol;
+        const uint16_t* p = Vp + row * D + ((((col >> 3) ^ vswz<D>(row)) << 3) | (col & 7));
+        part[e2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+      }
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    if constexpr (do_qk) {
+      S[0] = f32x16{};
+      S[1] = f32x16{};
+    }
+    bf16x8 fr[kLook];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kt + (kt * 32 + l32) * D + (((2 * s + hi) ^ kx) * 8));
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
+    for (int j = 0; j < kLook && j < NOPS; ++j) fr[j] = load(j);
+#pragma unroll
+    for (int j = 0; j < NOPS; ++j) {
+      const bf16x8 f = fr[j % kLook];
+      if (j + kLook < NOPS) fr[j % kLook] = load(j + kLook);
+      if (is_qk(j)) {
+        const int q = sub(j), st = q >> 1, kt = q & 1;
+        S[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[st], S[kt], 0, 0, 0);
+      } else {
+        const int q = sub(j), kt = q / (2 * DT), h2 = (q / DT) & 1, dt = q % DT;
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[kt][h2], oacc[dt], 0, 0, 0);
       }
     }
-    float mx = -INFINITY;
+  };
+
+  // vector phase: online softmax of the current sub-block (scores S, block validity ok). The running
+  // maximum is only refreshed when the exponentials overflow a bound: P = 2^(c s - m_run) is computed
+  // first, and when any lane's partial sum exceeds kSumMax (or is not finite, as on the first block,
+  // where m_run = -inf) the row maximum is taken, O and l are rescaled and P is recomputed.
+  auto exps = [&](float neg_m) __attribute__((always_inline)) -> float {
+    float x[2][16];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
-    mx = ok ? fmaxf(mx, __shfl_xor(mx, 32)) * a.c : -INFINITY;  // c > 0
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyMax)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      for (int v = 0; v < 16; ++v) x[kt][v] = __builtin_fmaf(S[kt][v], a.c, neg_m);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x[kt][v] = __builtin_amdgcn_exp2f(x[kt][v]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[kt][h2][e] = (__bf16)x[kt][8 * h2 + e];
+    // row sum of the rounded probabilities that P V uses: bf16 pair dot products with (1, 1)
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 w = pf[u >> 1][u & 1];
+        acc[u] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[e], w[e + 1]}, ones, acc[u], false);
+      }
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  };
+  auto vphase = [&](bool ok) __attribute__((always_inline)) {
+    float ls = exps(ok ? -m_run : -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(!(ls <= kSumMax))) {
+      const float mxs = ok ? tile_rowmax(S) * a.c : -INFINITY;
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+      ls = exps(ok ? -m_run : -INFINITY);
     }
-    const float neg_m = ok ? -m_run : -INFINITY;
-    float ls = 0.f;
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * h2 + e], a.c, neg_m));
-          ls += pv;
-          pf[kt][h2][e] = (__bf16)pv;
-        }
     l_run += ls;
-
-    // O^T += V^T P^T; k-slot 8*hi + e of step (kt, h2) is key kt*32 + 16*h2 + 8*(e/4) + 4*hi + e%4
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          v4i16 part[2];
-#pragma unroll
-          for (int e2 = 0; e2 < 2; ++e2) {
-            const int row = kt * 32 + 16 * h2 + 8 * e2 + vrow;
-            const int col = dt * 32 + vcol;
-            const uint16_t* p = Vt + row * D + ((((col >> 3) ^ vswz<D>(row)) << 3) | (col & 7));
-            part[e2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
-          }
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kt][h2], oacc[dt], 0, 0, 0);
-        }
   };
-  for (int m = 0; m < total; m += 2) {
-    step(m, buf0, buf1);
-    if (m + 1 < total) step(m + 1, buf1, buf0);
+
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  // one kept block n: sub-blocks m = 2n (frame 0) and m = 2n + 1 (frame 1); MORE: block n + 1 exists
+  auto block_iter = [&](int n, auto more_tag) __attribute__((always_inline)) {
+    constexpr bool MORE = decltype(more_tag)::value;
+    const int jn = n + 3 < nsel ? sel[n + 3] : 0;  // entry of block n + 3, needed two blocks later
+    // ---- vector phase of m = 2n
+    if constexpr (MORE) issue_tile<D, false>(krs, kb0, kst, base_n, g.W, lwave, lane);  // K(n+1, 0)
+    issue_tile<D, true>(vrs, vb1, vst, base_c + hw, g.W, lwave, lane);                 // V(n, 1)
+    vphase(ok_c);
+    wait_tiles<LOADS>(MORE ? 2 : 1);  // K(n, 1) and V(n, 0) have landed
+    phase_barrier();
+    ++phase;
+    mphase(vb0, kb1, Yes{}, Yes{});  // P V(n, 0); S = K(n, 1) Q^T
+    phase_barrier();
+    ++phase;
+    // ---- vector phase of m = 2n + 1
+    if constexpr (MORE) {
+      issue_tile<D, false>(krs, kb1, kst, base_n + hw, g.W, lwave, lane);  // K(n+1, 1)
+      issue_tile<D, true>(vrs, vb0, vst, base_n, g.W, lwave, lane);        // V(n+1, 0)
+    }
+    vphase(ok_c);
+    wait_tiles<LOADS>(MORE ? 2 : 0);  // K(n+1, 0) and V(n, 1) have landed
+    phase_barrier();
+    ++phase;
+    if constexpr (MORE) {
+      mphase(vb1, kb0, Yes{}, Yes{});  // P V(n, 1); S = K(n+1, 0) Q^T
+    } else {
+      mphase(vb1, kb0, Yes{}, No{});
+    }
+    phase_barrier();
+    ++phase;
+    ok_c = ok_n;
+    base_c = base_n;
+    base_n = block_base(j_pref, ok_n);
+    j_pref = jn;
+  };
+
+  if (t > 0) {
+    mphase(vb1, kb0, No{}, Yes{});  // M(0): S = K(0, 0) Q^T
+    phase_barrier();
+    ++phase;
+    for (int n = 0; n + 1 < nsel; ++n) block_iter(n, Yes{});
+    block_iter(nsel - 1, No{});
+  }
+  while (phase < phases) {
+    phase_barrier();
+    ++phase;
   }
 
+  if (!has) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   uint16_t* ob = static_cast<uint16_t*>(a.o) + b * a.osb + h * a.osh + int64_t(qtok) * a.ost;
@@ -539,6 +673,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_direct_kernel(AttnArgs a) {
     const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     a.lse[int64_t(bh) * a.nq_tok + qtok] = lse;
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnArgs a) {
+  constexpr int TE = Tile<D>::ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t k00[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t k01[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t v00[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t v01[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t k10[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t k11[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t v10[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t v11[TE];
+
+  // XCD-aware order over workgroups (hardware deals workgroup n to XCD n % 8)
+  const int nwg = a.nwg;
+  int wg = blockIdx.x;
+  const int n8 = (nwg / 8) * 8;
+  if (wg < n8) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int nblocks = a.nrows;
+  const int q0 = 2 * wg, q1 = 2 * wg + 1;
+  const const_i32* rp = (const const_i32*)(a.row_ptr);
+  const int i0 = q0 % a.g.nqb, i1 = q1 % a.g.nqb;
+  const int r0 = rp[i0], n0 = rp[i0 + 1] - r0;
+  const int r1 = q1 < nblocks ? rp[i1] : 0, n1 = q1 < nblocks ? rp[i1 + 1] - r1 : 0;
+  const int G = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+  const int lwave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);
+  if (G == 0)
+    pp_group<D>(a, 0, q0, r0, n0, n1, lwave, k00, k01, v00, v01);
+  else
+    pp_group<D>(a, 1, q1 < nblocks ? q1 : -1, r1, n1, n0, lwave, k10, k11, v10, v11);
 }
 
 }  // namespace
@@ -581,11 +746,15 @@ extern "C" lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_
   a.c = static_cast<float>(static_cast<double>(p->scale) * 1.4426950408889634);
   a.k_span = static_cast<uint32_t>((hw * p->kv_frames - 1) * ks.token * esz + p->head_dim * esz);
   a.v_span = static_cast<uint32_t>((hw * p->kv_frames - 1) * vs.token * esz + p->head_dim * esz);
+  a.div_bpt = make_fastdiv(static_cast<uint32_t>(g.bpt));
+  a.div_wb = make_fastdiv(static_cast<uint32_t>(g.Wb));
+  a.nrows = p->batch * p->heads * g.nqb;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (p->dtype == LCSA_BF16) {
-    if (p->head_dim == 128) attn_fwd_direct_kernel<128><<<a.nwg, 256, 0, s>>>(a);
-    else attn_fwd_direct_kernel<64><<<a.nwg, 256, 0, s>>>(a);
+    a.nwg = (a.nrows + 1) / 2;  // two query blocks per workgroup
+    if (p->head_dim == 128) attn_fwd_pp_kernel<128><<<a.nwg, 512, 0, s>>>(a);
+    else attn_fwd_pp_kernel<64><<<a.nwg, 512, 0, s>>>(a);
   } else {
     if (p->head_dim == 128) attn_fwd_kernel<float, 128><<<a.nwg, 256, 0, s>>>(a);
     else attn_fwd_kernel<float, 64><<<a.nwg, 256, 0, s>>>(a);

@@ -74,6 +74,24 @@ LCSA_HD int qblock_window(const Geom& g, int i, int* h0, int* h1, int* w0, int* 
   return tb;
 }
 
+// Unsigned division by a run-time constant d >= 1 as one multiply and a shift (Granlund-Montgomery
+// round-up method): with l = ceil(log2 d), k = 32 + l and M = ceil(2^k / d), floor(n / d) equals
+// floor(n * M / 2^k) for every n < 2^31 (M <= 2^33, so the product fits in 64 bits).
+struct FastDiv {
+  uint64_t m;
+  uint32_t k;
+  uint32_t d;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t p = uint64_t(1) << (32 + l);
+  return FastDiv{(p + d - 1) / d, 32 + l, d};
+}
+
+LCSA_HD uint32_t fast_div(uint32_t n, const FastDiv& f) { return uint32_t((uint64_t(n) * f.m) >> f.k); }
+
 LCSA_HD int n_visible(const Geom& g, int i) {
   int h0, h1, w0, w1;
   const int tb = qblock_window(g, i, &h0, &h1, &w0, &w1);

@@ -97,6 +97,11 @@ EDGE = [
     W.Workload("d128_f32", 1, 2, 128, 16, 24, 4, 2, 2, dtype="f32", keep_ratio=0.5),
     # the largest key count a selection row holds (1188 key blocks, 18 temporal blocks)
     W.Workload("max_keys_768x1408_kv36", 1, 1, 128, 48, 88, 36, 34, 2, keep_ratio=0.05),
+    # an odd number of (batch, head, query block) rows: the last workgroup's second query block is
+    # empty; with a truncated window the two rows of a workgroup keep different block counts
+    W.Workload("odd_rows_24x40", 1, 1, 128, 24, 40, 4, 2, 2, keep_ratio=0.4),
+    W.Workload("odd_rows_24x40_win_trunc", 1, 1, 128, 24, 40, 4, 2, 2, win_mode=1, win_h=24, win_w=24, keep_ratio=0.5),
+    W.Workload("odd_rows_24x40_d64", 1, 3, 64, 24, 40, 2, 0, 2, keep_ratio=0.4),
 ]
 
 

@@ -56,6 +56,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=0,
                     help="query blocks per head in the oracle sample (0 = all)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one captured HIP graph of the three calls per step instead of eager launches "
+                         "(measured no faster on this path: the launches are already queued ahead)")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3 counter runs: warmup + `steps` steps, then one plain device copy "
                          "of 256 MiB (the byte-counter calibration kernel); prints a short line")
@@ -90,7 +93,6 @@ def main():
     col = torch.empty((w.batch, w.heads, nnz), dtype=torch.int32, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((w.batch, w.heads, w.nq_tokens), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
 
     pairs = w.batch * w.heads * nnz
     flop = pairs * 4.0 * 128 * 128 * w.head_dim
@@ -99,6 +101,8 @@ def main():
     sel_bytes = w.batch * w.heads * ((nqb + nkb) * w.head_dim * 4 + nnz * 4)
 
     def step(ev=None):
+        # every call goes to the current stream (the capture stream while a graph is recorded)
+        stream = torch.cuda.current_stream()
         if ev:
             ev[0].record(stream)
         lcsa.lcsa_pool(p, q, k, qp, kp, stream=stream)
@@ -115,6 +119,21 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # optionally, one step captured as a HIP graph and replayed
+    run_step = step
+    if args.graph and not args.profile:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run_step = graph.replay
+
     if args.profile:
         for _ in range(args.steps):
             step()
@@ -128,9 +147,10 @@ def main():
         return
 
     # whole-step timing: K back-to-back steps between two synchronisations
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -168,6 +188,7 @@ def main():
                    "topk": w.topk or None, "window": ["none", "truncated", "preserving"][w.win_mode],
                    "selected_pairs": pairs, "selected_gflop": round(flop / 1e9, 2)},
         "ms_per_chunk": round(ms_per_step, 4),
+        "launch": "eager" if run_step is step else "hip_graph",
         "kernels_ms_median": {"lcsa_pool": round(med(t_pool), 4), "lcsa_score_select": round(med(t_sel), 4),
                               "lcsa_attn_fwd": round(med(t_attn), 4), "step_events": round(med(t_step_ev), 4)},
         "pool_gbs": round(pool_bytes / (med(t_pool) * 1e-3) / 1e9, 1),

@@ -16,6 +16,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 #include "lcsa_internal.h"
 
 namespace lcsa {
@@ -176,12 +178,25 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
   }
 }
 
+// The dynamic-LDS limit of each kernel instantiation is raised once per device (to the largest
+// size a row can need), not on every call, so that launches can be captured into a HIP graph.
+constexpr int kMaxDevices = 64;
+
 template <int D, int SLOTS>
 lcsa_status launch(const SelArgs& a, int wgs, size_t lds, hipStream_t s) {
-  lcsa_status st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<D, SLOTS>),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)),
-                              "lcsa_score_select LDS size");
+  static std::atomic<uint64_t> raised[kMaxDevices];
+  int dev = 0;
+  lcsa_status st = hip_status(hipGetDevice(&dev), "lcsa_score_select device");
   if (st != LCSA_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(LCSA_ERR_UNSUPPORTED, "lcsa_score_select: device %d", dev);
+  if (raised[dev].load(std::memory_order_acquire) == 0) {
+    const size_t max_lds = size_t(kRows) * (((kMaxCols + 15) / 16) * 16 + kLdsPad) * sizeof(double);
+    st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<D, SLOTS>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(max_lds)),
+                    "lcsa_score_select LDS size");
+    if (st != LCSA_OK) return st;
+    raised[dev].store(1, std::memory_order_release);
+  }
   score_select_kernel<D, SLOTS><<<wgs, kThreads, lds, s>>>(a);
   return LCSA_OK;
 }

@@ -49,6 +49,18 @@ __device__ __forceinline__ bool is_visible(const Geom& g, int tbi, int h0, int h
   return tbj <= tbi && hb >= h0 && hb <= h1 && wb >= w0 && wb <= w1;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (lane order), with DPP row shifts inside each
+// 16-lane row and row broadcasts across rows.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15 into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 __device__ __forceinline__ uint64_t order_key(double s) {
   const uint64_t u = static_cast<uint64_t>(__double_as_longlong(s == 0.0 ? 0.0 : s));
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
@@ -145,19 +157,42 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
     int need = min(K, ncand);
     uint64_t prefix = 0, mask = 0;
     int eq = ncand;  // candidates whose masked key equals the prefix
-    for (int bit = 63; bit >= 0 && eq != need; --bit) {
-      const uint64_t bm = uint64_t(1) << bit;
-      int cnt1 = 0;
+    // Most-significant-digit-first radix select, 8-bit digits: per digit, a histogram (this wave's
+    // score row, no longer needed, serves as 256 counters) of the candidates that match the prefix,
+    // a suffix scan from the largest digit and the digit where the K_i-th largest key lies.
+    uint32_t* hist = reinterpret_cast<uint32_t*>(S + rl * a.ld);
 #pragma unroll
-      for (int m = 0; m < SLOTS; ++m) cnt1 += __popcll(__ballot(((key[m] & mask) == prefix) & ((key[m] & bm) != 0)));
-      if (cnt1 >= need) {
-        prefix |= bm;
-        eq = cnt1;
-      } else {
-        need -= cnt1;
-        eq -= cnt1;
+    for (int k = 0; k < 4; ++k) hist[4 * lane + k] = 0;
+    for (int shift = 56; shift >= 0 && eq != need; shift -= 8) {
+#pragma unroll
+      for (int m = 0; m < SLOTS; ++m)
+        if (key[m] != 0 && (key[m] & mask) == prefix) atomicAdd(&hist[(key[m] >> shift) & 255], 1u);
+      // lane L holds digits 255 - 4L - k, k = 0..3 (descending)
+      uint32_t c[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[k] = hist[255 - 4 * lane - k];
+      const int tot = int(c[0] + c[1] + c[2] + c[3]);
+      const int incl = wave_inclusive_sum(tot);  // candidates with digit >= 252 - 4L
+      const uint64_t reach = __ballot(incl >= need);
+      const int L = __builtin_ctzll(reach);       // first lane whose range holds the need-th key
+      int above = __shfl(incl - tot, L);          // candidates with a larger digit than lane L's
+      int d = 255 - 4 * L, cnt = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int ck = __shfl(int(c[k]), L);
+        if (cnt == 0 && above + ck >= need) {
+          d = 255 - 4 * L - k;
+          cnt = ck;
+        } else if (cnt == 0) {
+          above += ck;
+        }
       }
-      mask |= bm;
+      need -= above;
+      eq = cnt;
+      prefix |= uint64_t(d) << shift;
+      mask |= uint64_t(255) << shift;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) hist[4 * lane + k] = 0;
     }
     // kept: masked key above the prefix, or equal to it and among the first `need` such (by j);
     // key 0 is never kept (a kept key is at least the K-th largest candidate key, which is > 0)
@@ -225,6 +260,7 @@ extern "C" lcsa_status lcsa_score_select(const lcsa_problem* p, const float* q_p
   if ((st = lcsa_csr_layout(p, nullptr, nullptr, &nnz, nullptr)) != LCSA_OK) return st;
   SelArgs a{q_pooled, k_pooled, row_ptr, col_idx, scores_dbg, g, nnz, 0, static_cast<double>(p->scale)};
   a.ld = ((g.nkb + 15) / 16) * 16 + kLdsPad;
+  if (a.ld < 128) a.ld = 128;  // a row also holds the 256 radix counters of its selection
   const size_t lds = size_t(kRows) * a.ld * sizeof(double);
   const int wgs = p->batch * p->heads * ((g.nqb + kRows - 1) / kRows);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -30,6 +30,10 @@ The passages leave several steps open; the readings taken here (all stated in DE
      so every query keeps w_b blocks per axis when the grid has that many.
   R7 the pooled feature is the arithmetic mean of the block's 128 tokens.
 Every function works in fp64 on exact copies of the kernel inputs.
+
+The backward (`attend_bwd`) is not described by the sources: it is the exact gradient of `attend`
+for a fixed selection, written out from the definition of softmax attention (the selection
+itself is discrete and not differentiated).
 """
 from __future__ import annotations
 
@@ -196,6 +200,47 @@ def attend(p, q, k, v, row_ptr, col_idx, qblocks=None, bh=None):
             O[b, h, qt] = (e / den) @ v[b, h, kt]
             lse[b, h, qt] = (m + np.log(den))[:, 0]
     return O, lse
+
+
+def attend_bwd(p, q, k, v, row_ptr, col_idx, dO, qblocks=None, bh=None):
+    """Gradients of `attend` for a fixed selection: given dL/dO, returns dL/dQ, dL/dK, dL/dV (fp64).
+
+    The selection (row_ptr, col_idx) is an input, not differentiated. For each query token t of block
+    i and the tokens k of its kept blocks, with logits s = scale*q.k, P = softmax(s) and O = P V:
+      dV_k += sum_t P_tk dO_t,  dP_tk = dO_t . v_k,  Delta_t = dO_t . O_t = sum_k P_tk dP_tk,
+      dS_tk = P_tk (dP_tk - Delta_t),  dQ_t = scale sum_k dS_tk k_k,  dK_k += scale sum_t dS_tk q_t.
+    dK and dV sum over every query block that kept the key block. With `qblocks` only those query
+    blocks contribute (dQ of the other rows stays NaN).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    qb, kb = query_blocks(p), key_blocks(p)
+    dQ = np.full(q.shape, np.nan)
+    dK = np.zeros(k.shape)
+    dV = np.zeros(v.shape)
+    qblocks = range(len(qb)) if qblocks is None else qblocks
+    B, Hh = q.shape[:2]
+    bh = [(b, h) for b in range(B) for h in range(Hh)] if bh is None else bh
+    ktok = [block_tokens(p, blk, 0) for blk in kb]
+    for i in qblocks:
+        qt = block_tokens(p, qb[i], p.q_frame0)
+        for b, h in bh:
+            sel = col_idx[b, h, row_ptr[i]:row_ptr[i + 1]]
+            kt = np.concatenate([ktok[j] for j in sel])
+            logits = p.scale * (q[b, h, qt] @ k[b, h, kt].T)
+            e = np.exp(logits - logits.max(axis=1, keepdims=True))
+            P = e / e.sum(axis=1, keepdims=True)                    # [128, n]
+            Ot = P @ v[b, h, kt]
+            g = dO[b, h, qt]
+            dP = g @ v[b, h, kt].T
+            delta = (g * Ot).sum(axis=1, keepdims=True)
+            dS = P * (dP - delta)
+            dQ[b, h, qt] = p.scale * (dS @ k[b, h, kt])
+            dK[b, h, kt] += p.scale * (dS.T @ q[b, h, qt])
+            dV[b, h, kt] += P.T @ g
+    return dQ, dK, dV
 
 
 def forward(p, q, k, v, qblocks=None, bh=None):

@@ -1,0 +1,615 @@
+// lcsa_attn_bwd: gradients of the block-sparse attention (lcsa_attn_fwd) for a fixed selection.
+// Stage 2 of FlashVSR trains the sparse-causal model with block-sparse attention (FlashVSR summary,
+// sec. 2.2); training needs these gradients. For query token t of block i, the tokens k of its
+// kept blocks, s = scale q.k, P = softmax(s) (recomputed from the forward's lse) and upstream dO:
+//   dV_k += sum_t P_tk dO_t;  dP_tk = dO_t . v_k;  Delta_t = dO_t . O_t;  dS_tk = P_tk (dP_tk - Delta_t)
+//   dQ_t = scale sum_k dS_tk k_k;  dK_k += scale sum_t dS_tk q_t.
+// Kernels:
+//   delta: Delta_t for every query token (fp32).
+//   csc:   per (batch, head), the transpose of the selection: for every key block the ascending list
+//          of query blocks that kept it.
+//   dq:    per (batch, head, query block), like the forward: 4 waves of 32 query rows, S^T = K Q^T and
+//          dP^T = V dO^T as bf16 MFMAs, dS^T in fp32, dQ^T += K^T dS^T with dS^T rounded to bf16.
+//   dkdv:  per (batch, head, key block), over its query-block list: 4 waves of 32 key rows,
+//          S = Q K^T and dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.
+// Every gradient element is written by exactly one workgroup, in a fixed order: results are
+// deterministic and need no atomics.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "lcsa_internal.h"
+
+namespace lcsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+constexpr int kTok = 64;                // tokens per tile: one latent frame of a 2x8x8 block
+constexpr int kBufDword3 = 0x00020000;  // raw 32-bit buffer data format
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  int64_t qsb, qsh, qst, ksb, ksh, kst, vsb, vsh, vst, osb, osh, ost, dsb, dsh, dst;  // element strides
+  const float* lse;        // [B*Hh, Nq] natural-log softmax denominators of the forward
+  const int32_t* row_ptr;  // [nqb + 1]
+  const int32_t* col_idx;  // [B*Hh, nnz], ascending per row
+  float* dq;               // [B*Hh, Nq, d]
+  float* dk;               // [B*Hh, Nk, d]
+  float* dv;               // [B*Hh, Nk, d]
+  float* delta;            // workspace [B*Hh, Nq]
+  int32_t* col_ptr;        // workspace [B*Hh, nkb + 1]
+  int32_t* row_of;         // workspace [B*Hh, nnz]
+  Geom g;
+  int32_t heads, nnz, nq_tok, nk_tok;
+  float c;                 // scale * log2(e)
+  float scale;
+  uint32_t q_span, k_span, v_span, do_span;  // bytes of one (batch, head) slice
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufDword3);
+}
+
+// Token index of row r (0..127) of block (tr, hb, wb), tr relative to the tensor's first temporal block.
+__device__ __forceinline__ int block_token(const Geom& g, int tr, int hb, int wb, int r) {
+  return ((kBlkT * tr + (r >> 6)) * g.H + kBlkH * hb + ((r >> 3) & 7)) * g.W + kBlkW * wb + (r & 7);
+}
+
+// First token of block j (frame 0), for a tensor whose first temporal block is temporal block 0.
+__device__ __forceinline__ uint32_t block_base(const Geom& g, int j) {
+  const int tr = j / g.bpt, rem = j - (j / g.bpt) * g.bpt;
+  const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
+  return uint32_t((kBlkT * tr * g.H + kBlkH * hb) * g.W + kBlkW * wb);
+}
+
+// A tile is 64 tokens x D bf16 in LDS, row-major; 16-byte chunk c of row r sits at chunk c ^ (r mod CPR)
+// (row-fragment reads of 16 consecutive rows hit distinct banks). Loads go straight to LDS.
+template <int D>
+struct TileB {
+  static constexpr int CPR = D / 8;
+  static constexpr int LOADS = kTok * CPR / 256;  // 16-byte loads per lane (256 lanes)
+  static constexpr int ELEMS = kTok * D;
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* tile, uint32_t tst, uint32_t base_tok,
+                                          int W) {
+  constexpr int CPR = TileB<D>::CPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int it = 0; it < TileB<D>::LOADS; ++it) {
+    const int slot0 = (wave * TileB<D>::LOADS + it) * 64;
+    const int r0 = slot0 / CPR;
+    const int r = r0 + lane / CPR;
+    const int c = (lane % CPR) ^ (r & (CPR - 1));
+    const uint32_t soff = (base_tok + uint32_t((r0 / 8) * W + (r0 % 8))) * tst * 2u;
+    const uint32_t voff = (uint32_t(lane / CPR) * tst + 8u * uint32_t(c)) * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(tile + slot0 * 8), 16, voff, soff, 0, 0);
+  }
+}
+
+// Row fragment: tile rows t*32 + l32, d = 16*s + 8*hi .. +8 (an MFMA A operand, or a B operand).
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const uint16_t* tile, int t, int s) {
+  constexpr int CPR = D / 8;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  const int r = t * 32 + l32;
+  return *reinterpret_cast<const bf16x8*>(tile + r * D + (((2 * s + hi) ^ (r & (CPR - 1))) * 8));
+}
+
+// Transposed fragment: A operand [32 d x 16 tokens] of an MFMA whose k index runs over tile rows in
+// the permuted order k-slot 8*hi + e <-> row t*32 + 16*h2 + 8*(e/4) + 4*hi + e%4 (the order in which
+// a 32x32 score accumulator holds its rows), for d tile dt. Read with ds_read_b64_tr_b16.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int t, int h2, int dt) {
+  constexpr int CPR = D / 8;
+  const int lane = threadIdx.x & 63, hi = lane >> 5, jj = lane & 15;
+  const int vrow = 4 * hi + jj / 4, vcol = (lane & 16) + 4 * (jj & 3);
+  v4i16 part[2];
+#pragma unroll
+  for (int e2 = 0; e2 < 2; ++e2) {
+    const int row = t * 32 + 16 * h2 + 8 * e2 + vrow;
+    const int col = dt * 32 + vcol;
+    const uint16_t* p = tile + row * D + ((((col >> 3) ^ (row & (CPR - 1))) << 3) | (col & 7));
+    part[e2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  }
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Packs a 32x32 fp32 accumulator (rows in the MFMA result order) into two bf16 B operands whose
+// k-slots follow the permuted order of tr_frag: half h2 holds items 8*h2 .. 8*h2 + 7.
+__device__ __forceinline__ void pack_b(const f32x16& x, bf16x8 (&out)[2]) {
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[h2][e] = (__bf16)x[8 * h2 + e];
+}
+
+// ---------------------------------------------------------------------------------------- delta
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(BwdArgs a, int64_t ntok) {
+  constexpr int LPT = D / 8;             // lanes per token (8 elements each)
+  constexpr int TPB = 256 / LPT;         // tokens per workgroup
+  const int64_t t = int64_t(blockIdx.x) * TPB + threadIdx.x / LPT;
+  const int c = threadIdx.x % LPT;
+  float acc = 0.f;
+  if (t < ntok) {
+    const int64_t bh = t / a.nq_tok, n = t - bh * a.nq_tok;
+    const int b = int(bh / a.heads), h = int(bh - (bh / a.heads) * a.heads);
+    const uint4 ov = *reinterpret_cast<const uint4*>(a.o + b * a.osb + h * a.osh + n * a.ost + 8 * c);
+    const uint4 gv = *reinterpret_cast<const uint4*>(a.dout + b * a.dsb + h * a.dsh + n * a.dst + 8 * c);
+    const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc = __builtin_fmaf(__uint_as_float(ow[k] << 16), __uint_as_float(gw[k] << 16), acc);
+      acc = __builtin_fmaf(__uint_as_float(ow[k] & 0xffff0000u), __uint_as_float(gw[k] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int o = LPT / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (t < ntok && c == 0) a.delta[t] = acc;
+}
+
+// ------------------------------------------------------------------------------------------ csc
+// One workgroup per (batch, head). The kept (row, column) pairs of a range of columns are marked in
+// an LDS bitmap stored column-major (column c owns words [c*wq, (c+1)*wq), bit i = query block i);
+// each thread then counts and lists its own contiguous run of columns, so every list comes out in
+// ascending row order whatever order the marks were set in.
+constexpr int kCscWords = 16384;  // 64 KB bitmap
+
+__global__ __launch_bounds__(1024) void csc_kernel(BwdArgs a) {
+  __shared__ uint32_t bits[kCscWords];
+  __shared__ int32_t part[1024];
+  const Geom& g = a.g;
+  const int bh = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int32_t* col = a.col_idx + int64_t(bh) * a.nnz;
+  int32_t* cp = a.col_ptr + int64_t(bh) * (g.nkb + 1);
+  int32_t* ro = a.row_of + int64_t(bh) * a.nnz;
+  const int wq = (g.nqb + 31) / 32;  // bitmap words per column (the host checks wq <= kCscWords)
+  const int cw = kCscWords / wq;     // columns per pass
+  if (threadIdx.x == 0) cp[0] = 0;
+  int base = 0;                      // entries listed by earlier passes
+  for (int c0 = 0; c0 < g.nkb; c0 += cw) {
+    const int nc = min(cw, g.nkb - c0);
+    for (int w = threadIdx.x; w < nc * wq; w += 1024) bits[w] = 0;
+    __syncthreads();
+    // one wave per query block, lanes over its kept entries
+    for (int i = wave; i < g.nqb; i += 16) {
+      const int rb = a.row_ptr[i], re = a.row_ptr[i + 1];
+      for (int e = rb + lane; e < re; e += 64) {
+        const int c = col[e] - c0;
+        if (c >= 0 && c < nc) atomicOr(&bits[c * wq + (i >> 5)], 1u << (i & 31));
+      }
+    }
+    __syncthreads();
+    const int per = (nc + 1023) / 1024;
+    const int cb = min(int(threadIdx.x) * per, nc), ce = min(cb + per, nc);
+    int cnt = 0;
+    for (int c = cb; c < ce; ++c)
+      for (int w = 0; w < wq; ++w) cnt += __popc(bits[c * wq + w]);
+    // inclusive scan of the per-thread counts (Hillis-Steele over 1024 entries)
+    part[threadIdx.x] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int x = int(threadIdx.x) >= off ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += x;
+      __syncthreads();
+    }
+    int run = base + part[threadIdx.x] - cnt;
+    const int pass_total = part[1023];
+    for (int c = cb; c < ce; ++c) {
+      for (int w = 0; w < wq; ++w) {
+        uint32_t m = bits[c * wq + w];
+        while (m) {
+          ro[run++] = 32 * w + __builtin_ctz(m);
+          m &= m - 1;
+        }
+      }
+      cp[c0 + c + 1] = run;
+    }
+    base += pass_total;
+    __syncthreads();  // the next pass clears the bitmap and reuses part
+  }
+}
+
+// ------------------------------------------------------------------------------------------- dq
+template <int D>
+__global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
+  constexpr int DS = D / 16, DT = D / 32;
+  constexpr int TE = TileB<D>::ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t kt0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t vt0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t kt1[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t vt1[TE];
+  const Geom& g = a.g;
+  const int bh = blockIdx.x / g.nqb, i = blockIdx.x - (blockIdx.x / g.nqb) * g.nqb;
+  const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
+  const int qhb = qrem / g.Wb, qwb = qrem - (qrem / g.Wb) * g.Wb;
+  const int qtok = block_token(g, qtr, qhb, qwb, 32 * wave + l32);
+
+  bf16x8 qf[DS], gf[DS];  // B operands: this lane's query row, d = 16*s + 8*hi .. +8
+  {
+    const uint16_t* qs = a.q + b * a.qsb + h * a.qsh + int64_t(qtok) * a.qst + 8 * hi;
+    const uint16_t* gs = a.dout + b * a.dsb + h * a.dsh + int64_t(qtok) * a.dst + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      qf[s] = *reinterpret_cast<const bf16x8*>(qs + 16 * s);
+      gf[s] = *reinterpret_cast<const bf16x8*>(gs + 16 * s);
+    }
+  }
+  const float lse2 = a.lse[int64_t(bh) * a.nq_tok + qtok] * 1.4426950408889634f;
+  const float dlt = a.delta[int64_t(bh) * a.nq_tok + qtok];
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + b * a.ksb + h * a.ksh, a.k_span);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + b * a.vsb + h * a.vsh, a.v_span);
+  const uint32_t kst = uint32_t(a.kst), vst = uint32_t(a.vst);
+  const uint32_t hw = uint32_t(g.H) * uint32_t(g.W);
+  const int beg = a.row_ptr[i], nsel = a.row_ptr[i + 1] - beg;
+  const int32_t* sel = a.col_idx + int64_t(bh) * a.nnz + beg;
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+
+  // sub-tile m = frame m%2 of entry m/2; invalid entries load block 0 and contribute nothing
+  auto base_of = [&](int m, bool& ok) -> uint32_t {
+    const int j = sel[m >> 1];
+    ok = j >= 0 && j < g.nkb;
+    return block_base(g, ok ? j : 0) + uint32_t(m & 1) * hw;
+  };
+  auto step = [&](const uint16_t* Kt, const uint16_t* Vt, bool ok) __attribute__((always_inline)) {
+    f32x16 st[2], pt[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = f32x16{};
+      pt[t] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Kt, t, s), qf[s], st[t], 0, 0, 0);
+        pt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Vt, t, s), gf[s], pt[t], 0, 0, 0);
+      }
+    }
+    // dS^T = P^T (dP^T - Delta), P^T = exp2(c s - lse2); a skipped entry gives dS = 0
+    const float neg = ok ? -lse2 : -INFINITY;
+    bf16x8 dsf[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x16 d;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][v], a.c, neg));
+        d[v] = p * (pt[t][v] - dlt);
+      }
+      pack_b(d, dsf[t]);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(Kt, t, h2, dt), dsf[t][h2], acc[dt], 0, 0, 0);
+  };
+
+  const int total = 2 * nsel;
+  bool ok_n = false;
+  if (total > 0) {
+    const uint32_t b0 = base_of(0, ok_n);
+    load_tile<D>(krs, kt0, kst, b0, g.W);
+    load_tile<D>(vrs, vt0, vst, b0, g.W);
+  }
+  for (int m = 0; m < total; m += 2) {
+    bool ok = ok_n;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    {
+      const uint32_t bn = base_of(m + 1, ok_n);
+      load_tile<D>(krs, kt1, kst, bn, g.W);
+      load_tile<D>(vrs, vt1, vst, bn, g.W);
+    }
+    step(kt0, vt0, ok);
+    ok = ok_n;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (m + 2 < total) {
+      const uint32_t bn = base_of(m + 2, ok_n);
+      load_tile<D>(krs, kt0, kst, bn, g.W);
+      load_tile<D>(vrs, vt0, vst, bn, g.W);
+    }
+    step(kt1, vt1, ok);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  float* out = a.dq + (int64_t(bh) * a.nq_tok + qtok) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = dt * 32 + 8 * g4 + 4 * hi;
+      *reinterpret_cast<float4*>(out + d0) =
+          make_float4(acc[dt][4 * g4] * a.scale, acc[dt][4 * g4 + 1] * a.scale, acc[dt][4 * g4 + 2] * a.scale,
+                      acc[dt][4 * g4 + 3] * a.scale);
+    }
+}
+
+// ----------------------------------------------------------------------------------------- dkdv
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv_kernel(BwdArgs a) {
+  constexpr int DS = D / 16, DT = D / 32;
+  constexpr int TE = TileB<D>::ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t qt0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t gt0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t qt1[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t gt1[TE];
+  __shared__ __attribute__((aligned(16))) float rl0[2][kTok];  // [lse2 | delta] of the tile's queries
+  __shared__ __attribute__((aligned(16))) float rl1[2][kTok];
+  const Geom& g = a.g;
+  const int bh = blockIdx.x / g.nkb, j = blockIdx.x - (blockIdx.x / g.nkb) * g.nkb;
+  const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int ktr = j / g.bpt, krem = j - (j / g.bpt) * g.bpt;
+  const int khb = krem / g.Wb, kwb = krem - (krem / g.Wb) * g.Wb;
+  const int ktok = block_token(g, ktr, khb, kwb, 32 * wave + l32);
+
+  bf16x8 kf[DS], vf[DS];  // B operands: this lane's key row
+  {
+    const uint16_t* ks = a.k + b * a.ksb + h * a.ksh + int64_t(ktok) * a.kst + 8 * hi;
+    const uint16_t* vs = a.v + b * a.vsb + h * a.vsh + int64_t(ktok) * a.vst + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      kf[s] = *reinterpret_cast<const bf16x8*>(ks + 16 * s);
+      vf[s] = *reinterpret_cast<const bf16x8*>(vs + 16 * s);
+    }
+  }
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + b * a.qsb + h * a.qsh, a.q_span);
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + b * a.dsb + h * a.dsh, a.do_span);
+  const uint32_t qst = uint32_t(a.qst), dst = uint32_t(a.dst);
+  const uint32_t hw = uint32_t(g.H) * uint32_t(g.W);
+  const int32_t* cp = a.col_ptr + int64_t(bh) * (g.nkb + 1);
+  const int beg = cp[j], nrow = cp[j + 1] - beg;
+  const int32_t* rows = a.row_of + int64_t(bh) * a.nnz + beg;
+  const float* lse_bh = a.lse + int64_t(bh) * a.nq_tok;
+  const float* dl_bh = a.delta + int64_t(bh) * a.nq_tok;
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+
+  // sub-tile m = frame m%2 of query block rows[m/2]; Q is stored from the query block's own frames
+  auto qbase_of = [&](int m) -> uint32_t {
+    const int i = rows[m >> 1];
+    const int tr = i / g.bpt, rem = i - (i / g.bpt) * g.bpt;
+    const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
+    return uint32_t((kBlkT * tr * g.H + kBlkH * hb) * g.W + kBlkW * wb) + uint32_t(m & 1) * hw;
+  };
+  auto load_rows = [&](int m, float (*rl)[kTok]) {
+    // lse (log2 units) and delta of the tile's 64 queries, in tile row order
+    if (threadIdx.x < kTok) {
+      const int r = threadIdx.x;
+      const uint32_t tok = qbase_of(m) + uint32_t((r >> 3) * g.W + (r & 7));
+      rl[0][r] = lse_bh[tok] * 1.4426950408889634f;
+      rl[1][r] = dl_bh[tok];
+    }
+  };
+  auto step = [&](const uint16_t* Qt, const uint16_t* Gt, const float (*rl)[kTok]) __attribute__((always_inline)) {
+    f32x16 sc[2], dp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sc[t] = f32x16{};
+      dp[t] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Qt, t, s), kf[s], sc[t], 0, 0, 0);
+        dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Gt, t, s), vf[s], dp[t], 0, 0, 0);
+      }
+    }
+    // item v of tile t is query row t*32 + (v/4)*8 + 4*hi + v%4 of the sub-tile
+    bf16x8 pb[2][2], db[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x16 p, ds;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = t * 32 + g4 * 8 + 4 * hi;
+        const float4 l4 = *reinterpret_cast<const float4*>(&rl[0][r0]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&rl[1][r0]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * g4 + e;
+          p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.c, -lv[e]));
+          ds[v] = p[v] * (dp[t][v] - dv4[e]);
+        }
+      }
+      pack_b(p, pb[t]);
+      pack_b(ds, db[t]);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(Gt, t, h2, dt), pb[t][h2], dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(Qt, t, h2, dt), db[t][h2], dk[dt], 0, 0, 0);
+        }
+  };
+
+  const int total = 2 * nrow;
+  if (total > 0) {
+    const uint32_t b0 = qbase_of(0);
+    load_tile<D>(qrs, qt0, qst, b0, g.W);
+    load_tile<D>(grs, gt0, dst, b0, g.W);
+    load_rows(0, rl0);
+  }
+  for (int m = 0; m < total; m += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    {
+      const uint32_t bn = qbase_of(m + 1);
+      load_tile<D>(qrs, qt1, qst, bn, g.W);
+      load_tile<D>(grs, gt1, dst, bn, g.W);
+      load_rows(m + 1, rl1);
+    }
+    step(qt0, gt0, rl0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (m + 2 < total) {
+      const uint32_t bn = qbase_of(m + 2);
+      load_tile<D>(qrs, qt0, qst, bn, g.W);
+      load_tile<D>(grs, gt0, dst, bn, g.W);
+      load_rows(m + 2, rl0);
+    }
+    step(qt1, gt1, rl1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  float* ok_ = a.dk + (int64_t(bh) * a.nk_tok + ktok) * D;
+  float* ov_ = a.dv + (int64_t(bh) * a.nk_tok + ktok) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = dt * 32 + 8 * g4 + 4 * hi;
+      *reinterpret_cast<float4*>(ok_ + d0) =
+          make_float4(dk[dt][4 * g4] * a.scale, dk[dt][4 * g4 + 1] * a.scale, dk[dt][4 * g4 + 2] * a.scale,
+                      dk[dt][4 * g4 + 3] * a.scale);
+      *reinterpret_cast<float4*>(ov_ + d0) =
+          make_float4(dv[dt][4 * g4], dv[dt][4 * g4 + 1], dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3]);
+    }
+}
+
+struct BwdLayout {
+  size_t delta, col_ptr, row_of, total;
+};
+
+BwdLayout bwd_layout(const lcsa_problem* p, const Geom& g, int32_t nnz) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t bhn = size_t(p->batch) * p->heads;
+  BwdLayout l{};
+  l.delta = 0;
+  l.col_ptr = up(bhn * size_t(g.nqb) * kBlkTokens * sizeof(float));
+  l.row_of = l.col_ptr + up(bhn * size_t(g.nkb + 1) * sizeof(int32_t));
+  l.total = l.row_of + up(bhn * size_t(nnz > 0 ? nnz : 1) * sizeof(int32_t));
+  return l;
+}
+
+}  // namespace
+}  // namespace lcsa
+
+using namespace lcsa;
+
+extern "C" lcsa_status lcsa_attn_bwd_workspace_size(const lcsa_problem* p, size_t* bytes) {
+  Geom g;
+  lcsa_status st = validate_problem(p, &g);
+  if (st != LCSA_OK) return st;
+  if (!bytes) return fail(LCSA_ERR_INVALID, "lcsa_attn_bwd_workspace_size: bytes is NULL");
+  int32_t nnz = 0;
+  if ((st = lcsa_csr_layout(p, nullptr, nullptr, &nnz, nullptr)) != LCSA_OK) return st;
+  *bytes = bwd_layout(p, g, nnz).total;
+  return LCSA_OK;
+}
+
+extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
+                                     lcsa_strides ks, const void* v, lcsa_strides vs, const void* o, lcsa_strides os,
+                                     const void* d_o, lcsa_strides dos, const float* lse, const int32_t* row_ptr,
+                                     const int32_t* col_idx, float* dq, float* dk, float* dv, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  Geom g;
+  lcsa_status st = validate_problem(p, &g);
+  if (st != LCSA_OK) return st;
+  if (p->dtype != LCSA_BF16) return fail(LCSA_ERR_UNSUPPORTED, "lcsa_attn_bwd: only bf16 inputs are implemented");
+  const int64_t hw = int64_t(p->grid_h) * p->grid_w;
+  if ((st = check_tensor("q", q, qs, p, hw * p->q_frames)) != LCSA_OK) return st;
+  if ((st = check_tensor("k", k, ks, p, hw * p->kv_frames)) != LCSA_OK) return st;
+  if ((st = check_tensor("v", v, vs, p, hw * p->kv_frames)) != LCSA_OK) return st;
+  if ((st = check_tensor("o", o, os, p, hw * p->q_frames)) != LCSA_OK) return st;
+  if ((st = check_tensor("d_o", d_o, dos, p, hw * p->q_frames)) != LCSA_OK) return st;
+  if (!lse || !row_ptr || !col_idx || !dq || !dk || !dv || !workspace)
+    return fail(LCSA_ERR_INVALID, "lcsa_attn_bwd: NULL lse, row_ptr, col_idx, gradient or workspace");
+  if (reinterpret_cast<uintptr_t>(lse) % 4 || reinterpret_cast<uintptr_t>(row_ptr) % 4 ||
+      reinterpret_cast<uintptr_t>(col_idx) % 4 || reinterpret_cast<uintptr_t>(dq) % 16 ||
+      reinterpret_cast<uintptr_t>(dk) % 16 || reinterpret_cast<uintptr_t>(dv) % 16 ||
+      reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(LCSA_ERR_INVALID, "lcsa_attn_bwd: misaligned lse, row_ptr, col_idx, gradient or workspace");
+  if ((g.nqb + 31) / 32 > kCscWords)
+    return fail(LCSA_ERR_UNSUPPORTED, "lcsa_attn_bwd: more than %d query blocks per head", 32 * kCscWords);
+  int32_t nnz = 0;
+  if ((st = lcsa_csr_layout(p, nullptr, nullptr, &nnz, nullptr)) != LCSA_OK) return st;
+  const BwdLayout l = bwd_layout(p, g, nnz);
+  if (workspace_bytes < l.total)
+    return fail(LCSA_ERR_INVALID, "lcsa_attn_bwd: workspace of %zu bytes, %zu needed", workspace_bytes, l.total);
+  const int64_t esz = 2;
+  auto span = [&](lcsa_strides s, int64_t ntok) { return (ntok - 1) * s.token * esz + p->head_dim * esz; };
+  if (span(qs, hw * p->q_frames) >= (int64_t(1) << 32) || span(ks, hw * p->kv_frames) >= (int64_t(1) << 32) ||
+      span(vs, hw * p->kv_frames) >= (int64_t(1) << 32) || span(dos, hw * p->q_frames) >= (int64_t(1) << 32))
+    return fail(LCSA_ERR_UNSUPPORTED, "lcsa_attn_bwd: a per-head tensor span exceeds 4 GiB");
+
+  BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(d_o);
+  a.qsb = qs.batch; a.qsh = qs.head; a.qst = qs.token;
+  a.ksb = ks.batch; a.ksh = ks.head; a.kst = ks.token;
+  a.vsb = vs.batch; a.vsh = vs.head; a.vst = vs.token;
+  a.osb = os.batch; a.osh = os.head; a.ost = os.token;
+  a.dsb = dos.batch; a.dsh = dos.head; a.dst = dos.token;
+  a.lse = lse;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  char* w = static_cast<char*>(workspace);
+  a.delta = reinterpret_cast<float*>(w + l.delta);
+  a.col_ptr = reinterpret_cast<int32_t*>(w + l.col_ptr);
+  a.row_of = reinterpret_cast<int32_t*>(w + l.row_of);
+  a.g = g;
+  a.heads = p->heads;
+  a.nnz = nnz;
+  a.nq_tok = static_cast<int32_t>(hw * p->q_frames);
+  a.nk_tok = static_cast<int32_t>(hw * p->kv_frames);
+  a.scale = p->scale;
+  a.c = static_cast<float>(static_cast<double>(p->scale) * 1.4426950408889634);
+  a.q_span = static_cast<uint32_t>(span(qs, hw * p->q_frames));
+  a.k_span = static_cast<uint32_t>(span(ks, hw * p->kv_frames));
+  a.v_span = static_cast<uint32_t>(span(vs, hw * p->kv_frames));
+  a.do_span = static_cast<uint32_t>(span(dos, hw * p->q_frames));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int bhn = p->batch * p->heads;
+  const int64_t ntok = int64_t(bhn) * a.nq_tok;
+  if (p->head_dim == 128) {
+    delta_kernel<128><<<int((ntok + 15) / 16), 256, 0, s>>>(a, ntok);
+  } else {
+    delta_kernel<64><<<int((ntok + 31) / 32), 256, 0, s>>>(a, ntok);
+  }
+  csc_kernel<<<bhn, 1024, 0, s>>>(a);
+  if (p->head_dim == 128) {
+    dq_kernel<128><<<bhn * g.nqb, 256, 0, s>>>(a);
+    dkdv_kernel<128><<<bhn * g.nkb, 256, 0, s>>>(a);
+  } else {
+    dq_kernel<64><<<bhn * g.nqb, 256, 0, s>>>(a);
+    dkdv_kernel<64><<<bhn * g.nkb, 256, 0, s>>>(a);
+  }
+  return hip_status(hipGetLastError(), "lcsa_attn_bwd launch");
+}

@@ -83,3 +83,11 @@ def make_inputs(w, seed: int = 0, want=("q", "k", "v")) -> dict:
     if w.dtype == "bf16":
         out = {k: bf16_bits(v) for k, v in out.items()}
     return out
+
+
+def make_grad(w, seed: int = 0) -> np.ndarray:
+    """Upstream gradient dL/dO for the backward: N(0,1) from rng([seed, 4]), [B, heads, Nq, d], as bf16
+    bit patterns (the workload's dtype is bf16 for every backward case)."""
+    g = np.random.default_rng([seed, 4]).standard_normal(
+        (w.batch, w.heads, w.q_frames * w.grid_h * w.grid_w, w.head_dim), dtype=np.float32)
+    return bf16_bits(g)

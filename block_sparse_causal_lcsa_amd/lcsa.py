@@ -1,8 +1,9 @@
 """Thin Python binding of liblcsa.so (ctypes). Argument marshalling only: every step of the LCSA
 forward runs in the library's HIP kernels; torch provides device memory and the stream.
 
-The functions carry the C names: lcsa_csr_layout, lcsa_pool, lcsa_score_select, lcsa_attn_fwd.
-`forward` chains the three device calls on the current stream.
+The functions carry the C names: lcsa_csr_layout, lcsa_pool, lcsa_score_select, lcsa_attn_fwd,
+lcsa_attn_bwd_workspace_size, lcsa_attn_bwd. `forward` chains the three forward device calls on the
+current stream.
 """
 from __future__ import annotations
 
@@ -18,6 +19,7 @@ LCSA_OK, LCSA_ERR_INVALID, LCSA_ERR_UNSUPPORTED, LCSA_ERR_HIP = 0, 1, 2, 3
 LCSA_BF16, LCSA_F32 = 0, 1
 
 EXPORTS = ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
+           "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd",
            "lcsa_status_string", "lcsa_last_error", "lcsa_version")
 
 
@@ -60,7 +62,11 @@ def load():
     lib.lcsa_pool.argtypes = [P, vp, S, vp, S, vp, vp, vp]
     lib.lcsa_score_select.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.lcsa_attn_fwd.argtypes = [P, vp, S, vp, S, vp, S, vp, vp, vp, S, vp, vp]
-    for f in ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd"):
+    lib.lcsa_attn_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.lcsa_attn_bwd.argtypes = [P, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, vp, vp, vp, vp,
+                                  ctypes.c_size_t, vp]
+    for f in ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
+              "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lcsa_status_string.argtypes = [ctypes.c_int]
     lib.lcsa_status_string.restype = ctypes.c_char_p
@@ -194,6 +200,40 @@ def lcsa_attn_fwd(p: LcsaProblem, q, k, v, row_ptr, col_idx, o=None, lse=None, w
     _check(load().lcsa_attn_fwd(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                 _ptr(row_ptr), _ptr(col_idx), _ptr(o), _strides(o), _ptr(lse), _stream(stream)))
     return o, lse
+
+
+def lcsa_attn_bwd_workspace_size(p: LcsaProblem) -> int:
+    """Bytes of device workspace lcsa_attn_bwd needs for this problem (host only)."""
+    n = ctypes.c_size_t()
+    _check(load().lcsa_attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def lcsa_attn_bwd(p: LcsaProblem, q, k, v, o, d_o, lse, row_ptr, col_idx, dq=None, dk=None, dv=None,
+                  workspace=None, stream=None):
+    """Gradients of lcsa_attn_fwd for a fixed selection -> (dq, dk, dv) fp32 device tensors."""
+    torch = _torch()
+    hw = p.grid_h * p.grid_w
+    nq, nk = p.q_frames * hw, p.kv_frames * hw
+    for name, t, n in (("q", q, nq), ("k", k, nk), ("v", v, nk), ("o", o, nq), ("d_o", d_o, nq)):
+        _check_token_tensor(name, t, p, n)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != p.batch * p.heads * nq:
+        raise ValueError("lse must be contiguous fp32 [B, Hh, Nq] (the forward's output)")
+    grads = []
+    for name, t, n in (("dq", dq, nq), ("dk", dk, nk), ("dv", dv, nk)):
+        if t is None:
+            t = torch.empty((p.batch, p.heads, n, p.head_dim), dtype=torch.float32, device=q.device)
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (p.batch, p.heads, n, p.head_dim):
+            raise ValueError(f"{name} must be contiguous fp32 [{p.batch}, {p.heads}, {n}, {p.head_dim}]")
+        grads.append(t)
+    need = lcsa_attn_bwd_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(load().lcsa_attn_bwd(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                _ptr(o), _strides(o), _ptr(d_o), _strides(d_o), _ptr(lse), _ptr(row_ptr),
+                                _ptr(col_idx), _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return tuple(grads)
 
 
 def forward(p: LcsaProblem, q, k, v, row_ptr=None, stream=None):

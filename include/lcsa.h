@@ -1,6 +1,6 @@
 /*
  * lcsa.h - C ABI of liblcsa.so: locality-constrained block-sparse causal attention (LCSA)
- * forward on AMD MI355X (gfx950).
+ * forward and backward on AMD MI355X (gfx950).
  *
  * The operation is the one described for FlashVSR's stage-2 sparse-causal attention and its
  * locality-constrained inference ("FlashVSR: Towards Real-time Diffusion-Based Streaming Video
@@ -29,6 +29,7 @@
 #ifndef LCSA_H_
 #define LCSA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -110,6 +111,29 @@ lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_strides qs,
                           lcsa_strides ks, const void* v, lcsa_strides vs, const int32_t* row_ptr,
                           const int32_t* col_idx, void* o, lcsa_strides os, float* lse,
                           void* stream);
+
+/* Gradients of lcsa_attn_fwd for a fixed selection (training the sparse-causal model, sec. 2.2
+ * "Stage 2": the attention is trained block-sparse; the Top-K selection itself is not
+ * differentiated). With P = softmax(scale * q K_S^T) over the kept blocks S of each query token's
+ * block and upstream gradient dO:
+ *   Delta = rowsum(dO * O); dP = dO V_S^T; dS = P * (dP - Delta)
+ *   dQ = scale * dS K_S;  dK_S += scale * dS^T Q;  dV_S += P^T dO
+ * dK and dV of a key block sum over every query block that kept it; key blocks nobody kept get 0.
+ * q, k, v, o, d_o: bf16 [B, Hh, N, d] with lcsa_strides (o, lse: the forward's outputs for the same
+ *   q, k, v and selection; d_o: dL/dO). row_ptr, col_idx: the selection, as lcsa_score_select
+ *   writes it (rows strictly ascending; entries outside [0, nkb) are skipped).
+ * dq: fp32 [B, Hh, Nq, d], dk, dv: fp32 [B, Hh, Nk, d], contiguous, 16-byte aligned, fully written.
+ * workspace: device memory of lcsa_attn_bwd_workspace_size bytes, 256-byte aligned, caller-owned,
+ *   no initial contents required; it must not be shared by calls that overlap in time.
+ * Arithmetic: bf16 MFMA with fp32 accumulation; P and dS rounded to bf16 for the dV, dK and dQ
+ * products; Delta in fp32 from the bf16 O. Deterministic: no atomics on the gradients.
+ * Only bf16 problems are implemented (LCSA_ERR_UNSUPPORTED otherwise). */
+lcsa_status lcsa_attn_bwd_workspace_size(const lcsa_problem* p, size_t* bytes);
+lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
+                          lcsa_strides ks, const void* v, lcsa_strides vs, const void* o,
+                          lcsa_strides os, const void* d_o, lcsa_strides dos, const float* lse,
+                          const int32_t* row_ptr, const int32_t* col_idx, float* dq, float* dk,
+                          float* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 const char* lcsa_status_string(lcsa_status s);
 const char* lcsa_last_error(void);   /* thread-local detail of this thread's last non-OK return */

@@ -118,6 +118,10 @@ def _check_rejected(w_or_p, status):
     assert lib.lcsa_pool(ctypes.byref(p), None, zs, None, zs, None, None, None) == status
     assert lib.lcsa_score_select(ctypes.byref(p), None, None, None, None, None, None) == status
     assert lib.lcsa_attn_fwd(ctypes.byref(p), None, zs, None, zs, None, zs, None, None, None, zs, None, None) == status
+    n = ctypes.c_size_t(0)
+    assert lib.lcsa_attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    assert lib.lcsa_attn_bwd(ctypes.byref(p), None, zs, None, zs, None, zs, None, zs, None, zs, None, None, None,
+                             None, None, None, None, 0, None) == status
 
 
 def test_bad_pointers_and_strides_rejected_on_host():
@@ -142,3 +146,34 @@ def test_bad_pointers_and_strides_rejected_on_host():
     big = BASE.replace(kv_frames=40, q_frame0=38)            # 1320 key blocks > one LDS row
     pb = lcsa.problem(big)
     assert lib.lcsa_score_select(ctypes.byref(pb), buf, buf, buf, buf, None, None) == lcsa.LCSA_ERR_UNSUPPORTED
+
+
+def test_backward_rejections_on_host():
+    lib = lcsa.load()
+    p = lcsa.problem(BASE)
+    d = BASE.head_dim
+    hw = BASE.grid_h * BASE.grid_w
+    qs = lcsa.LcsaStrides(12 * 2 * hw * d, 2 * hw * d, d)
+    ks = lcsa.LcsaStrides(12 * 6 * hw * d, 6 * hw * d, d)
+    buf = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    n = ctypes.c_size_t(0)
+    assert lib.lcsa_attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == lcsa.LCSA_OK
+    nqb, nkb, nnz, _ = lcsa.lcsa_csr_layout(p)
+    # delta [B*Hh*Nq] fp32, col_ptr [B*Hh*(nkb+1)] and row_of [B*Hh*nnz] int32, each 256-byte rounded
+    up = lambda x: (x + 255) // 256 * 256
+    assert n.value == up(12 * 2 * hw * 4) + up(12 * (nkb + 1) * 4) + up(12 * nnz * 4)
+    assert lib.lcsa_attn_bwd_workspace_size(ctypes.byref(p), None) == lcsa.LCSA_ERR_INVALID
+
+    def call(prob=p, lse=buf, ws=buf, wsb=n.value, dq=buf):
+        return lib.lcsa_attn_bwd(ctypes.byref(prob), buf, qs, buf, ks, buf, ks, buf, qs, buf, qs, lse, buf, buf,
+                                 dq, buf, buf, ws, wsb, None)
+
+    assert call(lse=None) == lcsa.LCSA_ERR_INVALID
+    assert call(ws=None) == lcsa.LCSA_ERR_INVALID
+    assert call(wsb=n.value - 1) == lcsa.LCSA_ERR_INVALID
+    assert b"workspace" in lib.lcsa_last_error()
+    assert call(dq=ctypes.c_void_p((1 << 20) + 8)) == lcsa.LCSA_ERR_INVALID
+    assert call(ws=ctypes.c_void_p((1 << 20) + 128)) == lcsa.LCSA_ERR_INVALID
+    pf = lcsa.problem(BASE.replace(dtype="f32"))
+    assert call(prob=pf) == lcsa.LCSA_ERR_UNSUPPORTED
+    assert b"bf16" in lib.lcsa_last_error()

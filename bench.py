@@ -59,6 +59,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph of the three calls per step instead of eager launches "
                          "(measured no faster on this path: the launches are already queued ahead)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time lcsa_attn_bwd (gradients for the selection of one forward) instead of the "
+                         "forward step; prints its own JSON line")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3 counter runs: warmup + `steps` steps, then one plain device copy "
                          "of 256 MiB (the byte-counter calibration kernel); prints a short line")
@@ -114,6 +117,10 @@ def main():
         lcsa.lcsa_attn_fwd(p, q, k, v, row_ptr, col, o, lse, stream=stream)
         if ev:
             ev[3].record(stream)
+
+    if args.backward:
+        backward_bench(args, w, p, x, dev, step, dict(q=q, k=k, v=v, o=o, lse=lse, row_ptr=row_ptr, col=col, nnz=nnz))
+        return
 
     for _ in range(args.warmup):
         step()
@@ -200,6 +207,64 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_sample_blocks)
+    print(json.dumps(out), flush=True)
+
+
+def backward_bench(args, w, p, x, dev, step, t):
+    """Times lcsa_attn_bwd on the selection, O and lse of one forward step (inputs resident in HBM).
+    FLOP per kept (head, i, j) pair: 5 products of 128 x 128 x d (S recomputed, dP, dV, dK, dQ), the
+    usual convention for attention backward; the kernels execute 7 (S and dP once in each of the dQ
+    and dK/dV kernels), reported as executed_tflops."""
+    import numpy as np
+    import torch
+
+    from block_sparse_causal_lcsa_amd import inputs, lcsa
+
+    step()
+    g = inputs.make_grad(w, seed=0)
+    d_o = torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).to(dev)
+    ws = torch.empty(lcsa.lcsa_attn_bwd_workspace_size(p), dtype=torch.uint8, device=dev)
+    hw = w.grid_h * w.grid_w
+    dq = torch.empty((w.batch, w.heads, w.q_frames * hw, w.head_dim), dtype=torch.float32, device=dev)
+    dk = torch.empty((w.batch, w.heads, w.kv_frames * hw, w.head_dim), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+
+    def bwd():
+        lcsa.lcsa_attn_bwd(p, t["q"], t["k"], t["v"], t["o"], d_o, t["lse"], t["row_ptr"], t["col"], dq, dk, dv,
+                           workspace=ws, stream=torch.cuda.current_stream())
+
+    for _ in range(args.warmup):
+        bwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        bwd()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        bwd()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    pairs = w.batch * w.heads * t["nnz"]
+    flop = pairs * 10.0 * 128 * 128 * w.head_dim
+    executed = pairs * 14.0 * 128 * 128 * w.head_dim
+    out = {
+        "metric": "LCSA attention backward effective TFLOP/s on selected blocks (5 GEMMs per kept pair)",
+        "value": round(flop / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: the forward's inputs; dO ~ N(0,1) rounded to bf16",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "grid": [w.grid_h, w.grid_w], "selected_pairs": pairs},
+        "roofline": {"bound": "mfma", "kernel": "lcsa_attn_bwd (delta, csc, dq, dkdv launches)",
+                     "achieved": round(executed / (call_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(executed / (call_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flop_per_launch": executed, "avg_launch_ms": round(call_ms, 4)},
+    }
     print(json.dumps(out), flush=True)
 
 

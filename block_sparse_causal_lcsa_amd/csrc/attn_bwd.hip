@@ -5,18 +5,22 @@
 //   dV_k += sum_t P_tk dO_t;  dP_tk = dO_t . v_k;  Delta_t = dO_t . O_t;  dS_tk = P_tk (dP_tk - Delta_t)
 //   dQ_t = scale sum_k dS_tk k_k;  dK_k += scale sum_t dS_tk q_t.
 // Kernels:
-//   delta: Delta_t for every query token (fp32).
+//   delta: Delta_t for every query token, and lse in log2 units (fp32, workspace).
 //   csc:   per (batch, head), the transpose of the selection: for every key block the ascending list
 //          of query blocks that kept it.
-//   dq:    per (batch, head, query block), like the forward: 4 waves of 32 query rows, S^T = K Q^T and
-//          dP^T = V dO^T as bf16 MFMAs, dS^T in fp32, dQ^T += K^T dS^T with dS^T rounded to bf16.
+//   dq:    per (batch, head, query block), like the forward: 4 waves of 32 query rows (two
+//          workgroups per CU), S^T = K Q^T and dP^T = V dO^T as bf16 MFMAs, dS^T in fp32,
+//          dQ^T += K^T dS^T with dS^T rounded to bf16. K/V sub-tiles double-buffered in LDS.
 //   dkdv:  per (batch, head, key block), over its query-block list: 4 waves of 32 key rows,
-//          S = Q K^T and dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.
+//          S = Q K^T and dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (P, dS rounded to bf16).
+//          Q/dO sub-tiles and their lse/Delta in a 3-stage LDS pipeline.
 // Every gradient element is written by exactly one workgroup, in a fixed order: results are
-// deterministic and need no atomics.
+// deterministic and need no atomics. All operand tiles go from memory straight into LDS.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <utility>
 
 #include "lcsa_internal.h"
 
@@ -43,7 +47,8 @@ struct BwdArgs {
   float* dq;               // [B*Hh, Nq, d]
   float* dk;               // [B*Hh, Nk, d]
   float* dv;               // [B*Hh, Nk, d]
-  float* delta;            // workspace [B*Hh, Nq]
+  float* delta;            // workspace [B*Hh, Nq]: rowsum(dO * O)
+  float* lse2;             // workspace [B*Hh, Nq]: lse * log2(e)
   int32_t* col_ptr;        // workspace [B*Hh, nkb + 1]
   int32_t* row_of;         // workspace [B*Hh, nnz]
   Geom g;
@@ -69,8 +74,17 @@ __device__ __forceinline__ uint32_t block_base(const Geom& g, int j) {
   return uint32_t((kBlkT * tr * g.H + kBlkH * hb) * g.W + kBlkW * wb);
 }
 
-// A tile is 64 tokens x D bf16 in LDS, row-major; 16-byte chunk c of row r sits at chunk c ^ (r mod CPR)
-// (row-fragment reads of 16 consecutive rows hit distinct banks). Loads go straight to LDS.
+// A tile is 64 tokens x D bf16 in LDS, row-major; 16-byte chunk c of row r sits at chunk c ^ swz(r).
+// Every tile is read two ways: row fragments (16 lanes on 16 consecutive rows, one chunk: needs swz
+// to be a bijection on each aligned run of 16 rows) and ds_read_b64_tr_b16 fragments (4 aligned
+// consecutive rows x 4 consecutive chunks per 32 lanes: needs the four swz values to differ in
+// their upper two bits). For D = 128, swz(r) = 4 (r mod 4) + (r / 4) mod 4 does both; for D = 64
+// (8 chunks per row) r mod 8 is used. Loads go straight to LDS.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (r & 7);
+}
+
 template <int D>
 struct TileB {
   static constexpr int CPR = D / 8;
@@ -82,13 +96,15 @@ template <int D>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* tile, uint32_t tst, uint32_t base_tok,
                                           int W) {
   constexpr int CPR = TileB<D>::CPR;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the scalar offset must be wave-uniform in registers the compiler can see as such
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  base_tok = __builtin_amdgcn_readfirstlane(base_tok);
 #pragma unroll
   for (int it = 0; it < TileB<D>::LOADS; ++it) {
     const int slot0 = (wave * TileB<D>::LOADS + it) * 64;
     const int r0 = slot0 / CPR;
     const int r = r0 + lane / CPR;
-    const int c = (lane % CPR) ^ (r & (CPR - 1));
+    const int c = (lane % CPR) ^ swz<D>(r);
     const uint32_t soff = (base_tok + uint32_t((r0 / 8) * W + (r0 % 8))) * tst * 2u;
     const uint32_t voff = (uint32_t(lane / CPR) * tst + 8u * uint32_t(c)) * 2u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -99,10 +115,9 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* t
 // Row fragment: tile rows t*32 + l32, d = 16*s + 8*hi .. +8 (an MFMA A operand, or a B operand).
 template <int D>
 __device__ __forceinline__ bf16x8 row_frag(const uint16_t* tile, int t, int s) {
-  constexpr int CPR = D / 8;
   const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
   const int r = t * 32 + l32;
-  return *reinterpret_cast<const bf16x8*>(tile + r * D + (((2 * s + hi) ^ (r & (CPR - 1))) * 8));
+  return *reinterpret_cast<const bf16x8*>(tile + r * D + (((2 * s + hi) ^ swz<D>(r)) * 8));
 }
 
 // Transposed fragment: A operand [32 d x 16 tokens] of an MFMA whose k index runs over tile rows in
@@ -110,7 +125,6 @@ __device__ __forceinline__ bf16x8 row_frag(const uint16_t* tile, int t, int s) {
 // a 32x32 score accumulator holds its rows), for d tile dt. Read with ds_read_b64_tr_b16.
 template <int D>
 __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int t, int h2, int dt) {
-  constexpr int CPR = D / 8;
   const int lane = threadIdx.x & 63, hi = lane >> 5, jj = lane & 15;
   const int vrow = 4 * hi + jj / 4, vcol = (lane & 16) + 4 * (jj & 3);
   v4i16 part[2];
@@ -118,7 +132,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int t, int h2, i
   for (int e2 = 0; e2 < 2; ++e2) {
     const int row = t * 32 + 16 * h2 + 8 * e2 + vrow;
     const int col = dt * 32 + vcol;
-    const uint16_t* p = tile + row * D + ((((col >> 3) ^ (row & (CPR - 1))) << 3) | (col & 7));
+    const uint16_t* p = tile + row * D + ((((col >> 3) ^ swz<D>(row)) << 3) | (col & 7));
     part[e2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
   }
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -131,6 +145,64 @@ __device__ __forceinline__ void pack_b(const f32x16& x, bf16x8 (&out)[2]) {
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[h2][e] = (__bf16)x[8 * h2 + e];
+}
+
+// Calls f(integral_constant<int, j>) for j = 0 .. N-1, fully unrolled with j a constant expression.
+template <class F, int... J>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Position of op j in the MFMA list of one 64-row sub-tile (two 32-row tiles t): group A (NA ops per
+// tile) and group B (NB ops per tile), ordered A(0) | LEAD ops of A(1) | the other A(1) ops evenly
+// interleaved with B(0) | B(1). The vector step of tile 0 goes before the interleaved part, that of
+// tile 1 before B(1).
+struct OpPos {
+  int grp, t, o;
+};
+template <int NA, int NB, int LEAD>
+constexpr OpPos op_pos(int j) {
+  constexpr int MIX0 = NA + LEAD, MIXN = NA - LEAD + NB;
+  if (j < NA) return {0, 0, j};
+  if (j < MIX0) return {0, 1, j - NA};
+  if (j < MIX0 + MIXN) {
+    const int k = j - MIX0, nb = (k * NB) / MIXN;  // B ops placed before position k
+    if (((k + 1) * NB) / MIXN > nb) return {1, 0, nb};
+    return {0, 1, LEAD + (k - nb)};
+  }
+  return {1, 1, j - MIX0 - MIXN};
+}
+
+// Wave-uniform 32-bit loads through the scalar cache (selection lists, row pointers).
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+// Workgroup barrier without a memory fence: direct-to-LDS loads still in flight stay in flight
+// (each wave waits for its own landed stages with vmcnt before). This wave's LDS reads are complete.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup order: hardware deals workgroup n to XCD n % 8; each XCD gets a contiguous range so that
+// neighbouring blocks of one head, which share most of their operands, share an L2.
+__device__ __forceinline__ int xcd_order() {
+  const int nwg = gridDim.x, n8 = (nwg / 8) * 8;
+  const int wg = blockIdx.x;
+  return wg < n8 ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
+}
+
+// Waits until at most `ahead` stages of PER vector-memory ops each are still in flight (ahead <= 3).
+template <int PER>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if (ahead >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
+  else if (ahead == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
+  else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------------------- delta
@@ -155,7 +227,10 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a, int64_t ntok) {
   }
 #pragma unroll
   for (int o = LPT / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  if (t < ntok && c == 0) a.delta[t] = acc;
+  if (t < ntok && c == 0) {
+    a.delta[t] = acc;
+    a.lse2[t] = a.lse[t] * 1.4426950408889634f;
+  }
 }
 
 // ------------------------------------------------------------------------------------------ csc
@@ -224,15 +299,13 @@ __global__ __launch_bounds__(1024) void csc_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------------------------------- dq
 template <int D>
-__global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(BwdArgs a) {
   constexpr int DS = D / 16, DT = D / 32;
   constexpr int TE = TileB<D>::ELEMS;
-  __shared__ __attribute__((aligned(16))) uint16_t kt0[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t vt0[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t kt1[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t vt1[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * TE];
   const Geom& g = a.g;
-  const int bh = blockIdx.x / g.nqb, i = blockIdx.x - (blockIdx.x / g.nqb) * g.nqb;
+  const int bh = xcd_order() / g.nqb, i = xcd_order() - bh * g.nqb;
   const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, hi = lane >> 5;
   const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
@@ -249,14 +322,15 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
       gf[s] = *reinterpret_cast<const bf16x8*>(gs + 16 * s);
     }
   }
-  const float lse2 = a.lse[int64_t(bh) * a.nq_tok + qtok] * 1.4426950408889634f;
+  const float lse2 = a.lse2[int64_t(bh) * a.nq_tok + qtok];
   const float dlt = a.delta[int64_t(bh) * a.nq_tok + qtok];
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + b * a.ksb + h * a.ksh, a.k_span);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + b * a.vsb + h * a.vsh, a.v_span);
   const uint32_t kst = uint32_t(a.kst), vst = uint32_t(a.vst);
   const uint32_t hw = uint32_t(g.H) * uint32_t(g.W);
-  const int beg = a.row_ptr[i], nsel = a.row_ptr[i + 1] - beg;
-  const int32_t* sel = a.col_idx + int64_t(bh) * a.nnz + beg;
+  const const_i32* rp = (const const_i32*)(a.row_ptr);
+  const int beg = rp[i], nsel = rp[i + 1] - beg;
+  const const_i32* sel = (const const_i32*)(a.col_idx) + int64_t(bh) * a.nnz + beg;
 
   f32x16 acc[DT];
 #pragma unroll
@@ -268,67 +342,55 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     ok = j >= 0 && j < g.nkb;
     return block_base(g, ok ? j : 0) + uint32_t(m & 1) * hw;
   };
+  // One 64-key sub-tile = two 32-key tiles t, one at a time: S^T = K Q^T and dP^T = V dO^T, the vector
+  // step dS^T = P^T (dP^T - Delta), then dQ^T += K^T dS^T. At two waves per SIMD the other wave fills
+  // the gaps; an explicit MFMA list with operands read ahead (as in the dK/dV kernel) needs more
+  // registers than two waves leave and was slower.
   auto step = [&](const uint16_t* Kt, const uint16_t* Vt, bool ok) __attribute__((always_inline)) {
-    f32x16 st[2], pt[2];
+    const float neg = ok ? -lse2 : -INFINITY;  // a skipped entry gives P = dS = 0
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      st[t] = f32x16{};
-      pt[t] = f32x16{};
+      f32x16 st = f32x16{}, pt = f32x16{};
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Kt, t, s), qf[s], st[t], 0, 0, 0);
-        pt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Vt, t, s), gf[s], pt[t], 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Kt, t, s), qf[s], st, 0, 0, 0);
+        pt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Vt, t, s), gf[s], pt, 0, 0, 0);
       }
-    }
-    // dS^T = P^T (dP^T - Delta), P^T = exp2(c s - lse2); a skipped entry gives dS = 0
-    const float neg = ok ? -lse2 : -INFINITY;
-    bf16x8 dsf[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
       f32x16 d;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][v], a.c, neg));
-        d[v] = p * (pt[t][v] - dlt);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.c, neg));
+        d[v] = p * (pt[v] - dlt);
       }
-      pack_b(d, dsf[t]);
-    }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
+      bf16x8 dsf[2];
+      pack_b(d, dsf);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(Kt, t, h2, dt), dsf[t][h2], acc[dt], 0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(Kt, t, h2, dt), dsf[h2], acc[dt], 0, 0, 0);
+    }
   };
 
+  // sub-tile m lives in buffer m % 2; the loads of m + 1 run while m is computed (two workgroups
+  // per CU hide the rest of the load latency)
   const int total = 2 * nsel;
-  bool ok_n = false;
+  bool ok_c = false, ok_n = false;
   if (total > 0) {
     const uint32_t b0 = base_of(0, ok_n);
-    load_tile<D>(krs, kt0, kst, b0, g.W);
-    load_tile<D>(vrs, vt0, vst, b0, g.W);
+    load_tile<D>(krs, kbuf, kst, b0, g.W);
+    load_tile<D>(vrs, vbuf, vst, b0, g.W);
   }
-  for (int m = 0; m < total; m += 2) {
-    bool ok = ok_n;
+  for (int m = 0; m < total; ++m) {
+    ok_c = ok_n;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    {
+    tile_barrier();
+    if (m + 1 < total) {
       const uint32_t bn = base_of(m + 1, ok_n);
-      load_tile<D>(krs, kt1, kst, bn, g.W);
-      load_tile<D>(vrs, vt1, vst, bn, g.W);
+      load_tile<D>(krs, kbuf + ((m + 1) & 1) * TE, kst, bn, g.W);
+      load_tile<D>(vrs, vbuf + ((m + 1) & 1) * TE, vst, bn, g.W);
     }
-    step(kt0, vt0, ok);
-    ok = ok_n;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (m + 2 < total) {
-      const uint32_t bn = base_of(m + 2, ok_n);
-      load_tile<D>(krs, kt0, kst, bn, g.W);
-      load_tile<D>(vrs, vt0, vst, bn, g.W);
-    }
-    step(kt1, vt1, ok);
+    step(kbuf + (m & 1) * TE, vbuf + (m & 1) * TE, ok_c);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -349,14 +411,13 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv_kernel(BwdArgs a) {
   constexpr int DS = D / 16, DT = D / 32;
   constexpr int TE = TileB<D>::ELEMS;
-  __shared__ __attribute__((aligned(16))) uint16_t qt0[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t gt0[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t qt1[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t gt1[TE];
-  __shared__ __attribute__((aligned(16))) float rl0[2][kTok];  // [lse2 | delta] of the tile's queries
-  __shared__ __attribute__((aligned(16))) float rl1[2][kTok];
+  constexpr int NBUF = 3;                          // stages: the loads of m + 1 and m + 2 run during m
+  constexpr int PER = 2 * TileB<D>::LOADS + 2;     // vector-memory ops per wave per stage
+  __shared__ __attribute__((aligned(16))) uint16_t qbuf[NBUF * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t gbuf[NBUF * TE];
+  __shared__ __attribute__((aligned(16))) float rlbuf[NBUF * 2 * kTok];  // per stage: [lse2 | delta] of its 64 queries
   const Geom& g = a.g;
-  const int bh = blockIdx.x / g.nkb, j = blockIdx.x - (blockIdx.x / g.nkb) * g.nkb;
+  const int bh = xcd_order() / g.nkb, j = xcd_order() - bh * g.nkb;
   const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, hi = lane >> 5;
   const int ktr = j / g.bpt, krem = j - (j / g.bpt) * g.bpt;
@@ -377,11 +438,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + b * a.dsb + h * a.dsh, a.do_span);
   const uint32_t qst = uint32_t(a.qst), dst = uint32_t(a.dst);
   const uint32_t hw = uint32_t(g.H) * uint32_t(g.W);
-  const int32_t* cp = a.col_ptr + int64_t(bh) * (g.nkb + 1);
+  const const_i32* cp = (const const_i32*)(a.col_ptr) + int64_t(bh) * (g.nkb + 1);
   const int beg = cp[j], nrow = cp[j + 1] - beg;
-  const int32_t* rows = a.row_of + int64_t(bh) * a.nnz + beg;
-  const float* lse_bh = a.lse + int64_t(bh) * a.nq_tok;
-  const float* dl_bh = a.delta + int64_t(bh) * a.nq_tok;
+  const const_i32* rows = (const const_i32*)(a.row_of) + int64_t(bh) * a.nnz + beg;
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.lse2 + int64_t(bh) * a.nq_tok, uint32_t(a.nq_tok) * 4u);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.delta + int64_t(bh) * a.nq_tok, uint32_t(a.nq_tok) * 4u);
 
   f32x16 dk[DT], dv[DT];
 #pragma unroll
@@ -397,88 +458,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
     return uint32_t((kBlkT * tr * g.H + kBlkH * hb) * g.W + kBlkW * wb) + uint32_t(m & 1) * hw;
   };
-  auto load_rows = [&](int m, float (*rl)[kTok]) {
-    // lse (log2 units) and delta of the tile's 64 queries, in tile row order
-    if (threadIdx.x < kTok) {
-      const int r = threadIdx.x;
-      const uint32_t tok = qbase_of(m) + uint32_t((r >> 3) * g.W + (r & 7));
-      rl[0][r] = lse_bh[tok] * 1.4426950408889634f;
-      rl[1][r] = dl_bh[tok];
+  // stage m: Q and dO tiles of sub-tile m, and lse2 / delta of its 64 queries (each wave 16 of them)
+  auto issue = [&](int m) {
+    const int sb = m % NBUF;
+    const uint32_t bn = __builtin_amdgcn_readfirstlane(qbase_of(m));
+    load_tile<D>(qrs, qbuf + sb * TE, qst, bn, g.W);
+    load_tile<D>(grs, gbuf + sb * TE, dst, bn, g.W);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    float* rl = rlbuf + sb * 2 * kTok + 16 * wv;
+    if (lane < 16) {
+      const int r = 16 * wv + lane;
+      const uint32_t voff = uint32_t((r >> 3) * g.W + (r & 7)) * 4u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (__attribute__((address_space(3))) void*)(rl), 4, voff,
+                                               bn * 4u, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)(rl + kTok), 4, voff,
+                                               bn * 4u, 0, 0);
     }
   };
-  auto step = [&](const uint16_t* Qt, const uint16_t* Gt, const float (*rl)[kTok]) __attribute__((always_inline)) {
+  // One 64-query sub-tile = two 32-query tiles t. Per tile: NA products S = Q K^T and dP = dO V^T
+  // (group A), the vector step P = 2^(c S - lse2), dS = P (dP - Delta), and NB products
+  // dV^T += dO^T P, dK^T += Q^T dS (group B), issued as one MFMA list (op_pos) whose LDS operands
+  // are read kLook MFMAs ahead.
+  auto step = [&](const uint16_t* Qt, const uint16_t* Gt, const float* rl) __attribute__((always_inline)) {
+    // LEAD = 0: the vector step of tile 0 follows A(0) directly (other orders and read-ahead depths
+    // from 4 to 8 measured within 3%)
+    constexpr int NA = 2 * DS, NB = 4 * DT, LEAD = 0, MIX0 = NA + LEAD, MIXN = NA - LEAD + NB;
+    constexpr int NOPS = 2 * NA + 2 * NB;
+    constexpr int kLook = 4;
     f32x16 sc[2], dp[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sc[t] = f32x16{};
-      dp[t] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Qt, t, s), kf[s], sc[t], 0, 0, 0);
-        dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Gt, t, s), vf[s], dp[t], 0, 0, 0);
-      }
-    }
-    // item v of tile t is query row t*32 + (v/4)*8 + 4*hi + v%4 of the sub-tile
     bf16x8 pb[2][2], db[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x16 p, ds;
+    // A op o: (o & 1) ? dP (dO, V) : S (Q, K), d step o / 2.
+    // B op o: (o & 1) ? dK (Q^T, dS) : dV (dO^T, P); d tile (o / 2) % DT, half (o / 2) / DT.
+    auto load = [&](auto jc) __attribute__((always_inline)) -> bf16x8 {
+      constexpr OpPos q = op_pos<NA, NB, LEAD>(decltype(jc)::value);
+      if constexpr (q.grp == 0) return row_frag<D>((q.o & 1) ? Gt : Qt, q.t, q.o >> 1);
+      else return tr_frag<D>((q.o & 1) ? Qt : Gt, q.t, (q.o >> 1) / DT, (q.o >> 1) % DT);
+    };
+    // item v of tile t is query row t*32 + (v/4)*8 + 4*hi + v%4 of the sub-tile
+    auto vec = [&](int t) __attribute__((always_inline)) {
+      f32x16 pv, ds;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int r0 = t * 32 + g4 * 8 + 4 * hi;
-        const float4 l4 = *reinterpret_cast<const float4*>(&rl[0][r0]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&rl[1][r0]);
+        const float4 l4 = *reinterpret_cast<const float4*>(rl + r0);
+        const float4 d4 = *reinterpret_cast<const float4*>(rl + kTok + r0);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = 4 * g4 + e;
-          p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.c, -lv[e]));
-          ds[v] = p[v] * (dp[t][v] - dv4[e]);
+          pv[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.c, -lv[e]));
+          ds[v] = pv[v] * (dp[t][v] - dv4[e]);
         }
       }
-      pack_b(p, pb[t]);
+      pack_b(pv, pb[t]);
       pack_b(ds, db[t]);
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(Gt, t, h2, dt), pb[t][h2], dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(Qt, t, h2, dt), db[t][h2], dk[dt], 0, 0, 0);
-        }
+    };
+    sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
+    bf16x8 fr[kLook];
+    static_for<kLook>([&](auto jc) __attribute__((always_inline)) { fr[decltype(jc)::value] = load(jc); });
+    static_for<NOPS>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      constexpr OpPos q = op_pos<NA, NB, LEAD>(j);
+      if constexpr (j == MIX0) vec(0);
+      if constexpr (j == MIX0 + MIXN) vec(1);
+      const bf16x8 f = fr[j % kLook];
+      if constexpr (j + kLook < NOPS) fr[j % kLook] = load(std::integral_constant<int, j + kLook>{});
+      if constexpr (q.grp == 0) {
+        if constexpr (q.o & 1) dp[q.t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, vf[q.o >> 1], dp[q.t], 0, 0, 0);
+        else sc[q.t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, kf[q.o >> 1], sc[q.t], 0, 0, 0);
+      } else {
+        constexpr int dt = (q.o >> 1) % DT, h2 = (q.o >> 1) / DT;
+        if constexpr (q.o & 1) dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, db[q.t][h2], dk[dt], 0, 0, 0);
+        else dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pb[q.t][h2], dv[dt], 0, 0, 0);
+      }
+    });
   };
 
+  // sub-tile m lives in stage buffer m % NBUF, loaded NBUF - 1 sub-tiles ahead
   const int total = 2 * nrow;
-  if (total > 0) {
-    const uint32_t b0 = qbase_of(0);
-    load_tile<D>(qrs, qt0, qst, b0, g.W);
-    load_tile<D>(grs, gt0, dst, b0, g.W);
-    load_rows(0, rl0);
+  for (int m = 0; m < NBUF - 1 && m < total; ++m) issue(m);
+  for (int m = 0; m < total; ++m) {
+    wait_stages<PER>(min(total - 1 - m, NBUF - 2));  // stage m has landed for this wave
+    tile_barrier();                                  // ... and for every wave; stage m - 1 is free
+    if (m + NBUF - 1 < total) issue(m + NBUF - 1);
+    const int sb = m % NBUF;
+    step(qbuf + sb * TE, gbuf + sb * TE, rlbuf + sb * 2 * kTok);
   }
-  for (int m = 0; m < total; m += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    {
-      const uint32_t bn = qbase_of(m + 1);
-      load_tile<D>(qrs, qt1, qst, bn, g.W);
-      load_tile<D>(grs, gt1, dst, bn, g.W);
-      load_rows(m + 1, rl1);
-    }
-    step(qt0, gt0, rl0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (m + 2 < total) {
-      const uint32_t bn = qbase_of(m + 2);
-      load_tile<D>(qrs, qt0, qst, bn, g.W);
-      load_tile<D>(grs, gt0, dst, bn, g.W);
-      load_rows(m + 2, rl0);
-    }
-    step(qt1, gt1, rl1);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   float* ok_ = a.dk + (int64_t(bh) * a.nk_tok + ktok) * D;
   float* ov_ = a.dv + (int64_t(bh) * a.nk_tok + ktok) * D;
@@ -496,7 +561,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 struct BwdLayout {
-  size_t delta, col_ptr, row_of, total;
+  size_t delta, lse2, col_ptr, row_of, total;
 };
 
 BwdLayout bwd_layout(const lcsa_problem* p, const Geom& g, int32_t nnz) {
@@ -504,7 +569,8 @@ BwdLayout bwd_layout(const lcsa_problem* p, const Geom& g, int32_t nnz) {
   const size_t bhn = size_t(p->batch) * p->heads;
   BwdLayout l{};
   l.delta = 0;
-  l.col_ptr = up(bhn * size_t(g.nqb) * kBlkTokens * sizeof(float));
+  l.lse2 = up(bhn * size_t(g.nqb) * kBlkTokens * sizeof(float));
+  l.col_ptr = l.lse2 + up(bhn * size_t(g.nqb) * kBlkTokens * sizeof(float));
   l.row_of = l.col_ptr + up(bhn * size_t(g.nkb + 1) * sizeof(int32_t));
   l.total = l.row_of + up(bhn * size_t(nnz > 0 ? nnz : 1) * sizeof(int32_t));
   return l;
@@ -580,6 +646,7 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
   a.dv = dv;
   char* w = static_cast<char*>(workspace);
   a.delta = reinterpret_cast<float*>(w + l.delta);
+  a.lse2 = reinterpret_cast<float*>(w + l.lse2);
   a.col_ptr = reinterpret_cast<int32_t*>(w + l.col_ptr);
   a.row_of = reinterpret_cast<int32_t*>(w + l.row_of);
   a.g = g;

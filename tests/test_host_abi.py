@@ -159,9 +159,9 @@ def test_backward_rejections_on_host():
     n = ctypes.c_size_t(0)
     assert lib.lcsa_attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == lcsa.LCSA_OK
     nqb, nkb, nnz, _ = lcsa.lcsa_csr_layout(p)
-    # delta [B*Hh*Nq] fp32, col_ptr [B*Hh*(nkb+1)] and row_of [B*Hh*nnz] int32, each 256-byte rounded
+    # delta and lse2 [B*Hh*Nq] fp32, col_ptr [B*Hh*(nkb+1)] and row_of [B*Hh*nnz] int32, each 256-byte rounded
     up = lambda x: (x + 255) // 256 * 256
-    assert n.value == up(12 * 2 * hw * 4) + up(12 * (nkb + 1) * 4) + up(12 * nnz * 4)
+    assert n.value == 2 * up(12 * 2 * hw * 4) + up(12 * (nkb + 1) * 4) + up(12 * nnz * 4)
     assert lib.lcsa_attn_bwd_workspace_size(ctypes.byref(p), None) == lcsa.LCSA_ERR_INVALID
 
     def call(prob=p, lse=buf, ws=buf, wsb=n.value, dq=buf):

@@ -62,6 +62,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time lcsa_attn_bwd (gradients for the selection of one forward) instead of the "
                          "forward step; prints its own JSON line")
+    ap.add_argument("--stream", type=int, default=0, metavar="CACHE",
+                    help="time chunk-by-chunk streaming with a K/V cache of CACHE temporal blocks "
+                         "(lcsa_stream_push + pool(q) + score_select + attn_fwd per chunk); prints its own JSON line")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3 counter runs: warmup + `steps` steps, then one plain device copy "
                          "of 256 MiB (the byte-counter calibration kernel); prints a short line")
@@ -78,6 +81,9 @@ def main():
     from block_sparse_causal_lcsa_amd import workloads as W
 
     w = W.BY_NAME[args.workload]
+    if args.stream:
+        stream_bench(args, w)
+        return
     p = lcsa.problem(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -266,6 +272,76 @@ def backward_bench(args, w, p, x, dev, step, t):
                      "traffic": None, "flop_per_launch": executed, "avg_launch_ms": round(call_ms, 4)},
     }
     print(json.dumps(out), flush=True)
+
+
+def stream_bench(args, w):
+    """Steady-state chunk time of streaming LCSA at the workload's frame size, heads and keep ratio:
+    a sequence of 8 temporal blocks resident in HBM is streamed through a cache of args.stream blocks
+    (cycling), every chunk = lcsa_stream_push(K, V of the new block) + lcsa_pool(q) + lcsa_score_select
+    + lcsa_attn_fwd on the cache window. Timing starts once the cache is full."""
+    import numpy as np
+    import torch
+
+    from block_sparse_causal_lcsa_amd import inputs, lcsa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nblk = 8
+    seq = w.replace(kv_frames=2 * nblk, q_frame0=0, q_frames=2 * nblk)
+    chunk = w.replace(kv_frames=2, q_frame0=0, q_frames=2)
+    x = inputs.make_inputs(seq, seed=0)
+    q, k, v = (torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in "qkv")
+    del x
+    tbt = 2 * w.grid_h * w.grid_w
+    views = [(q[:, :, c * tbt:(c + 1) * tbt], k[:, :, c * tbt:(c + 1) * tbt], v[:, :, c * tbt:(c + 1) * tbt])
+             for c in range(nblk)]
+    s = lcsa.Stream(lcsa.problem(chunk), args.stream)
+
+    def one(c, ev=None):
+        qc, kc, vc = views[c % nblk]
+        stream = torch.cuda.current_stream()
+        if ev:
+            ev[0].record(stream)
+        s.push(kc, vc, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        out = s.forward(qc, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        return out
+
+    c = 0
+    for _ in range(max(args.warmup, args.stream)):
+        one(c)
+        c += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = one(c)
+        c += 1
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        out = one(c, e)
+        c += 1
+    torch.cuda.synchronize()
+    push_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    fwd_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    pw = out["problem"]
+    nnz = int(out["row_ptr"][-1])
+    flop = w.batch * w.heads * nnz * 4.0 * 128 * 128 * w.head_dim
+    res = {
+        "metric": "LCSA streaming ms per chunk (push K/V + pool q + score_select + attn_fwd), cache full",
+        "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic: seeded smooth sinusoidal Q/K fields + 0.5 N(0,1), V ~ N(0,1)",
+        "config": {"workload": f"{w.name} streamed, cache {args.stream} temporal blocks", "heads": w.heads,
+                   "head_dim": w.head_dim, "grid": [w.grid_h, w.grid_w], "window_kv_frames": pw.kv_frames},
+        "kernels_ms_median": {"lcsa_stream_push": round(push_ms, 4), "pool_select_attn": round(fwd_ms, 4)},
+        "attention_tflops_per_chunk": round(flop / (ms * 1e-3) / 1e12, 2),
+    }
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(w, x, sample_blocks):

@@ -32,4 +32,11 @@ inline int dtype_size(const lcsa_problem* p) { return p->dtype == LCSA_F32 ? 4 :
 // Maps a HIP error to LCSA_ERR_HIP with its text; returns LCSA_OK for hipSuccess (0).
 lcsa_status hip_status(int err, const char* what);
 
+#if defined(__HIPCC__)
+// Block means of the key tensor k (all of p's key frames, validated by the caller) written to
+// out + ((b * heads + h) * out_rows + out_off + j) * head_dim for key block j (pool.hip).
+lcsa_status pool_k_into(const lcsa_problem* p, const Geom& g, const void* k, lcsa_strides ks, float* out,
+                        int32_t out_rows, int32_t out_off, hipStream_t s);
+#endif
+
 }  // namespace lcsa

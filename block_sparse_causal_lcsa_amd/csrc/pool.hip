@@ -16,9 +16,10 @@ namespace {
 struct PoolTensor {
   const void* x;
   int64_t sb, sh, st;  // element strides: batch, head, token
-  float* out;          // [B, Hh, nblk, d] fp32
+  float* out;          // block b of (batch, head) bh at row bh * out_rows + out_off + b, d floats each
   int32_t nblk;
   int32_t wgs;         // workgroups assigned to this tensor = B * Hh * nblk
+  int32_t out_rows, out_off;
 };
 
 template <typename T, int D>
@@ -76,7 +77,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolTensor ta, PoolTensor tb,
     double s = 0.0;
 #pragma unroll
     for (int k = 0; k < SLOTS; ++k) s += part[k][threadIdx.x];
-    t.out[(int64_t(bh) * t.nblk + blk) * D + threadIdx.x] = static_cast<float>(s * (1.0 / kBlkTokens));
+    t.out[(int64_t(bh) * t.out_rows + t.out_off + blk) * D + threadIdx.x] =
+        static_cast<float>(s * (1.0 / kBlkTokens));
   }
 }
 
@@ -86,6 +88,22 @@ void launch(const PoolTensor& a, const PoolTensor& b, int heads, const Geom& g, 
 }
 
 }  // namespace
+
+lcsa_status pool_k_into(const lcsa_problem* p, const Geom& g, const void* k, lcsa_strides ks, float* out,
+                        int32_t out_rows, int32_t out_off, hipStream_t s) {
+  PoolTensor tk{k, ks.batch, ks.head, ks.token, out, g.nkb, p->batch * p->heads * g.nkb, out_rows, out_off};
+  PoolTensor none{nullptr, 0, 0, 0, nullptr, 1, 0, 1, 0};
+  (void)hipGetLastError();
+  if (p->dtype == LCSA_BF16) {
+    if (p->head_dim == 128) launch<uint16_t, 128>(tk, none, p->heads, g, s);
+    else launch<uint16_t, 64>(tk, none, p->heads, g, s);
+  } else {
+    if (p->head_dim == 128) launch<float, 128>(tk, none, p->heads, g, s);
+    else launch<float, 64>(tk, none, p->heads, g, s);
+  }
+  return hip_status(hipGetLastError(), "pool launch");
+}
+
 }  // namespace lcsa
 
 using namespace lcsa;
@@ -97,8 +115,8 @@ extern "C" lcsa_status lcsa_pool(const lcsa_problem* p, const void* q, lcsa_stri
   if (st != LCSA_OK) return st;
   if (!q && !k) return fail(LCSA_ERR_INVALID, "lcsa_pool: q and k are both NULL");
   const int64_t hw = int64_t(p->grid_h) * p->grid_w;
-  PoolTensor tq{q, qs.batch, qs.head, qs.token, q_pooled, g.nqb, 0};
-  PoolTensor tk{k, ks.batch, ks.head, ks.token, k_pooled, g.nkb, 0};
+  PoolTensor tq{q, qs.batch, qs.head, qs.token, q_pooled, g.nqb, 0, g.nqb, 0};
+  PoolTensor tk{k, ks.batch, ks.head, ks.token, k_pooled, g.nkb, 0, g.nkb, 0};
   if (q) {
     if ((st = check_tensor("q", q, qs, p, hw * p->q_frames)) != LCSA_OK) return st;
     if (!q_pooled || reinterpret_cast<uintptr_t>(q_pooled) % 16)

@@ -20,6 +20,8 @@ LCSA_BF16, LCSA_F32 = 0, 1
 
 EXPORTS = ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
            "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd",
+           "lcsa_stream_state_size", "lcsa_stream_init", "lcsa_stream_reserve", "lcsa_stream_push",
+           "lcsa_stream_window",
            "lcsa_status_string", "lcsa_last_error", "lcsa_version")
 
 
@@ -32,6 +34,12 @@ class LcsaProblem(ctypes.Structure):
 
 class LcsaStrides(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
+class LcsaStream(ctypes.Structure):
+    _fields_ = [("chunk", LcsaProblem), ("cache_tblocks", ctypes.c_int32), ("ring_tblocks", ctypes.c_int32),
+                ("held", ctypes.c_int32), ("wpos", ctypes.c_int32), ("pushed", ctypes.c_int64),
+                ("mem", ctypes.c_void_p), ("mem_bytes", ctypes.c_size_t)]
 
 
 class LcsaError(RuntimeError):
@@ -65,8 +73,17 @@ def load():
     lib.lcsa_attn_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.lcsa_attn_bwd.argtypes = [P, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, vp, vp, vp, vp,
                                   ctypes.c_size_t, vp]
+    SP = ctypes.POINTER(LcsaStream)
+    lib.lcsa_stream_state_size.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.lcsa_stream_init.argtypes = [SP, P, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_size_t]
+    lib.lcsa_stream_reserve.argtypes = [SP, ctypes.POINTER(vp), ctypes.POINTER(S), ctypes.POINTER(vp),
+                                        ctypes.POINTER(S), vp]
+    lib.lcsa_stream_push.argtypes = [SP, vp, S, vp, S, vp]
+    lib.lcsa_stream_window.argtypes = [SP, P, ctypes.POINTER(vp), ctypes.POINTER(S), ctypes.POINTER(vp),
+                                       ctypes.POINTER(S), ctypes.POINTER(vp)]
     for f in ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
-              "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd"):
+              "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd", "lcsa_stream_state_size", "lcsa_stream_init",
+              "lcsa_stream_reserve", "lcsa_stream_push", "lcsa_stream_window"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lcsa_status_string.argtypes = [ctypes.c_int]
     lib.lcsa_status_string.restype = ctypes.c_char_p
@@ -245,3 +262,85 @@ def forward(p: LcsaProblem, q, k, v, row_ptr=None, stream=None):
     col = lcsa_score_select(p, qp, kp, row_ptr, stream=stream)
     o, lse = lcsa_attn_fwd(p, q, k, v, row_ptr, col, stream=stream)
     return dict(q_pooled=qp, k_pooled=kp, row_ptr=row_ptr, col_idx=col, o=o, lse=lse)
+
+
+# ------------------------------------------------------------------------------ streaming state
+def lcsa_stream_state_size(chunk: LcsaProblem, cache_tblocks: int, ring_tblocks: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().lcsa_stream_state_size(ctypes.byref(chunk), cache_tblocks, ring_tblocks, ctypes.byref(n)))
+    return n.value
+
+
+class Stream:
+    """Chunk-by-chunk LCSA with a K/V cache of the newest `cache_tblocks` temporal blocks (the C
+    lcsa_stream_* calls; device memory from torch). `push(k_new, v_new)` appends one temporal block;
+    `reserve()` gives the slot views a producer may write the next block into (then push those views:
+    no copy); `window()` returns the current chunk's problem and K, V, pooled-K tensor views into the
+    state; `forward(q)` runs lcsa_pool (q only) -> lcsa_score_select -> lcsa_attn_fwd on the window.
+    ring_tblocks defaults to 2 * cache_tblocks - 1 slots (compaction every cache_tblocks pushes)."""
+
+    def __init__(self, chunk: LcsaProblem, cache_tblocks: int, ring_tblocks: int = 0, device="cuda"):
+        torch = _torch()
+        self.chunk = chunk
+        ring = ring_tblocks or max(1, 2 * cache_tblocks - 1)
+        nbytes = lcsa_stream_state_size(chunk, cache_tblocks, ring)
+        self.mem = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.state = LcsaStream()
+        _check(load().lcsa_stream_init(ctypes.byref(self.state), ctypes.byref(chunk), cache_tblocks, ring,
+                                       _ptr(self.mem), nbytes))
+        self._rp = {}
+
+    def _view(self, ptr, st: LcsaStrides, ntok: int):
+        torch = _torch()
+        dt = _dtype(self.chunk)
+        esz = 4 if dt == torch.float32 else 2
+        c = self.chunk
+        return self.mem.view(dt).as_strided((c.batch, c.heads, ntok, c.head_dim), (st.batch, st.head, st.token, 1),
+                                            (ptr - self.mem.data_ptr()) // esz)
+
+    def reserve(self, stream=None):
+        """(k_slot, v_slot): tensor views of the ring slot the next pushed block occupies."""
+        kp, vp_ = ctypes.c_void_p(), ctypes.c_void_p()
+        ks, vs = LcsaStrides(), LcsaStrides()
+        _check(load().lcsa_stream_reserve(ctypes.byref(self.state), ctypes.byref(kp), ctypes.byref(ks),
+                                          ctypes.byref(vp_), ctypes.byref(vs), _stream(stream)))
+        n = 2 * self.chunk.grid_h * self.chunk.grid_w
+        return self._view(kp.value, ks, n), self._view(vp_.value, vs, n)
+
+    def push(self, k_new, v_new, stream=None):
+        hw2 = 2 * self.chunk.grid_h * self.chunk.grid_w
+        _check_token_tensor("k_new", k_new, self.chunk, hw2)
+        _check_token_tensor("v_new", v_new, self.chunk, hw2)
+        _check(load().lcsa_stream_push(ctypes.byref(self.state), _ptr(k_new), _strides(k_new), _ptr(v_new),
+                                       _strides(v_new), _stream(stream)))
+
+    def window(self):
+        """(problem, k, v, k_pooled): tensor views into the state, valid until the next push."""
+        torch = _torch()
+        p = LcsaProblem()
+        kp, vp_, kbp = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+        ks, vs = LcsaStrides(), LcsaStrides()
+        _check(load().lcsa_stream_window(ctypes.byref(self.state), ctypes.byref(p), ctypes.byref(kp),
+                                         ctypes.byref(ks), ctypes.byref(vp_), ctypes.byref(vs), ctypes.byref(kbp)))
+        base = self.mem.data_ptr()
+        nk = p.kv_frames * p.grid_h * p.grid_w
+        k = self._view(kp.value, ks, nk)
+        v = self._view(vp_.value, vs, nk)
+        _, nkb, _, _ = lcsa_csr_layout(p)
+        kbar = self.mem.view(torch.float32).as_strided((p.batch, p.heads, nkb, p.head_dim),
+                                                       (p.heads * nkb * p.head_dim, nkb * p.head_dim, p.head_dim, 1),
+                                                       (kbp.value - base) // 4)
+        return p, k, v, kbar
+
+    def forward(self, q, stream=None):
+        """The newest chunk's attention: q [B, Hh, 2*H*W, d] are its query frames."""
+        torch = _torch()
+        p, k, v, kbar = self.window()
+        key = p.kv_frames
+        if key not in self._rp:
+            self._rp[key] = torch.from_numpy(lcsa_csr_layout(p)[3]).to(q.device)
+        row_ptr = self._rp[key]
+        qp, _ = lcsa_pool(p, q, None, stream=stream)
+        col = lcsa_score_select(p, qp, kbar, row_ptr, stream=stream)
+        o, lse = lcsa_attn_fwd(p, q, k, v, row_ptr, col, stream=stream)
+        return dict(problem=p, q_pooled=qp, k_pooled=kbar, row_ptr=row_ptr, col_idx=col, o=o, lse=lse)

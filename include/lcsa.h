@@ -135,6 +135,61 @@ lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_strides qs,
                           const int32_t* row_ptr, const int32_t* col_idx, float* dq, float* dk,
                           float* dv, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Streaming state. FlashVSR processes video as a stream of chunks; the attention of a chunk reads
+ * the cached K/V of earlier chunks (fmread summary, sec. 2.2 Stage 3: temporal consistency is
+ * refined through the KV cache of later layers; sec. 3, efficiency analysis: streaming adds only an
+ * 8-frame lookahead, i.e. one temporal block of latent frames per chunk).
+ * The cache keeps the newest `cache_tblocks` temporal blocks (2 latent frames each) of K and V and
+ * the pooled K of those blocks, so each push pools only the new block's K.
+ *
+ * After the n-th push (w = min(n, cache_tblocks) blocks held), lcsa_stream_window describes the
+ * current chunk as an ordinary problem: kv_frames = 2w (the held blocks, oldest first),
+ * q_frame0 = 2(w - 1), q_frames = 2 (the newest block), and K, V, pooled K as device views into the
+ * state. lcsa_pool(q only), lcsa_score_select and lcsa_attn_fwd on that window give the chunk's
+ * output; they equal the same calls on K/V of the w newest blocks laid out contiguously, bit for
+ * bit. Blocks older than the window are evicted (invisible to later chunks).
+ *
+ * Memory: the caller allocates `mem` (device, 256-byte aligned, lcsa_stream_state_size bytes) and the
+ * lcsa_stream struct (host); the library keeps no other state. Inside `mem`: K and V rings of
+ * `ring_tblocks` (>= 2*cache_tblocks - 1) block slots per (batch, head), filled in order; the held
+ * blocks are always consecutive slots, so the window is one strided view. When the write position
+ * reaches the end, the newest cache_tblocks - 1 blocks are copied to the front (a larger ring makes
+ * this rarer: HBM capacity traded for bandwidth). Two pooled-K buffers are used alternately.
+ * Calls on one state must be ordered on one stream.
+ * chunk: batch, heads, head_dim, grid, window, topk/keep_ratio, scale, dtype of every chunk;
+ *        q_frames must be 2; kv_frames and q_frame0 are ignored. */
+typedef struct {
+  lcsa_problem chunk;
+  int32_t cache_tblocks;  /* >= 1 */
+  int32_t ring_tblocks;   /* >= max(1, 2 * cache_tblocks - 1) */
+  int32_t held;           /* blocks currently held, min(pushed, cache_tblocks) */
+  int32_t wpos;           /* ring slot the next block goes to (ring_tblocks: compaction due) */
+  int64_t pushed;         /* blocks pushed since init */
+  void* mem;
+  size_t mem_bytes;
+} lcsa_stream;
+
+lcsa_status lcsa_stream_state_size(const lcsa_problem* chunk, int32_t cache_tblocks, int32_t ring_tblocks,
+                                   size_t* bytes);
+/* Validates and resets *s (held = pushed = wpos = 0); no device work. */
+lcsa_status lcsa_stream_init(lcsa_stream* s, const lcsa_problem* chunk, int32_t cache_tblocks,
+                             int32_t ring_tblocks, void* mem, size_t mem_bytes);
+/* Device views [B, Hh, 2*H*W, d] of the ring slot the next pushed block occupies, so that a producer
+ * (e.g. the QKV projection) can write K and V there directly. Compacts the ring first when it is full
+ * (asynchronous on `stream`). Any of the outputs may be NULL. */
+lcsa_status lcsa_stream_reserve(lcsa_stream* s, void** k_slot, lcsa_strides* ks, void** v_slot,
+                                lcsa_strides* vs, void* stream);
+/* Appends one temporal block: k_new, v_new [B, Hh, 2*H*W, d] of the chunk's dtype (lcsa_strides as
+ * for lcsa_attn_fwd). When they are the views lcsa_stream_reserve returned, nothing is copied;
+ * otherwise they are copied into the slot. Pools k_new into the new pooled-K buffer after the kept
+ * part of the old one. Asynchronous on `stream`; *s is updated on the host at once. */
+lcsa_status lcsa_stream_push(lcsa_stream* s, const void* k_new, lcsa_strides ks, const void* v_new,
+                             lcsa_strides vs, void* stream);
+/* The current chunk as a problem and device views (valid until the next reserve or push). Fails
+ * with LCSA_ERR_INVALID before the first push. */
+lcsa_status lcsa_stream_window(const lcsa_stream* s, lcsa_problem* window, const void** k, lcsa_strides* ks,
+                               const void** v, lcsa_strides* vs, const float** k_pooled);
+
 const char* lcsa_status_string(lcsa_status s);
 const char* lcsa_last_error(void);   /* thread-local detail of this thread's last non-OK return */
 int32_t lcsa_version(void);          /* major*10000 + minor*100 + patch */

@@ -34,6 +34,12 @@ Every function works in fp64 on exact copies of the kernel inputs.
 The backward (`attend_bwd`) is not described by the sources: it is the exact gradient of `attend`
 for a fixed selection, written out from the definition of softmax attention (the selection
 itself is discrete and not differentiated).
+
+Streaming (`stream_forward`): the summary's sec. 2.2 Stage 3 refines temporal consistency through the
+KV cache, and sec. 3 (efficiency analysis) streams with an 8-frame lookahead. Reading R8: each chunk
+adds one temporal block (2 latent frames); the chunk's queries are that block and its keys/values
+are the cached blocks plus the new one, at most `cache_tblocks` blocks, older ones evicted. The chunk
+output is then the forward above on that window, with frames counted from the window's first frame.
 """
 from __future__ import annotations
 
@@ -251,6 +257,40 @@ def forward(p, q, k, v, qblocks=None, bh=None):
     row_ptr, col = select(p, s, vis)
     O, lse = attend(p, q, k, v, row_ptr, col, qblocks=qblocks, bh=bh)
     return dict(vis=vis, qbar=qbar, kbar=kbar, scores=s, row_ptr=row_ptr, col_idx=col, O=O, lse=lse)
+
+
+def stream_window(p, c: int, cache_tblocks: int):
+    """(first temporal block, problem) of streaming chunk c (0-based): the window holds temporal blocks
+    first..c, first = max(0, c - cache_tblocks + 1); the queries are block c (R8)."""
+    import copy
+    import dataclasses
+    first = max(0, c - cache_tblocks + 1)
+    w = c - first + 1
+    frames = dict(kv_frames=BLK_T * w, q_frame0=BLK_T * (w - 1), q_frames=BLK_T)
+    if dataclasses.is_dataclass(p):
+        return first, dataclasses.replace(p, **frames)
+    pw = copy.copy(p)
+    for name, val in frames.items():
+        setattr(pw, name, val)
+    return first, pw
+
+
+def stream_forward(p, q_seq, k_seq, v_seq, cache_tblocks: int, chunks=None):
+    """Chunk-by-chunk LCSA over a sequence (R8). q_seq, k_seq, v_seq: [B, heads, T*H*W, d], latent
+    frames 0..T-1 in raster order. Chunk c's queries are frames 2c, 2c+1; its keys and values are the
+    frames of `stream_window`. Returns {c: forward(...) of that window}."""
+    hw = p.grid_h * p.grid_w
+    tbt = BLK_T * hw
+    T = q_seq.shape[2] // hw
+    chunks = range(T // BLK_T) if chunks is None else chunks
+    out = {}
+    for c in chunks:
+        first, pw = stream_window(p, c, cache_tblocks)
+        q = q_seq[:, :, c * tbt:(c + 1) * tbt]
+        k = k_seq[:, :, first * tbt:(c + 1) * tbt]
+        v = v_seq[:, :, first * tbt:(c + 1) * tbt]
+        out[c] = forward(pw, q, k, v)
+    return out
 
 
 def dense_block_causal(p, q, k, v):

@@ -177,3 +177,78 @@ def test_backward_rejections_on_host():
     pf = lcsa.problem(BASE.replace(dtype="f32"))
     assert call(prob=pf) == lcsa.LCSA_ERR_UNSUPPORTED
     assert b"bf16" in lib.lcsa_last_error()
+
+
+def test_stream_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "slayout.c"
+    fields = [f[0] for f in lcsa.LcsaStream._fields_]
+    body = "".join(f'printf("%zu ", offsetof(lcsa_stream, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "lcsa.h"\n'
+                   f'int main(void){{ {body} printf("%zu\\n", sizeof(lcsa_stream)); return 0; }}\n')
+    exe = tmp_path / "slayout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    assert got[:-1] == [getattr(lcsa.LcsaStream, f).offset for f in fields]
+    assert got[-1] == ctypes.sizeof(lcsa.LcsaStream)
+
+
+def test_stream_state_on_host():
+    lib = lcsa.load()
+    chunk = BASE.replace(kv_frames=2, q_frame0=0, q_frames=2)
+    p = lcsa.problem(chunk)
+    n = ctypes.c_size_t(0)
+    assert lib.lcsa_stream_state_size(ctypes.byref(p), 3, 7, ctypes.byref(n)) == lcsa.LCSA_OK
+    # K and V rings of 7 temporal-block slots (bf16) + two pooled-K buffers of 3 blocks' means (fp32)
+    hw, d, Hh = BASE.grid_h * BASE.grid_w, BASE.head_dim, BASE.heads
+    blk = 2 * hw * d * 2                   # bytes of one temporal block of one head
+    ring = Hh * 7 * blk
+    kbar = Hh * 3 * (hw // 64) * d * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert n.value == 2 * up(ring) + 2 * up(kbar)
+    assert lib.lcsa_stream_state_size(ctypes.byref(p), 0, 7, ctypes.byref(n)) == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_stream_state_size(ctypes.byref(p), 3, 4, ctypes.byref(n)) == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_stream_state_size(ctypes.byref(p), 1, 1, ctypes.byref(n)) == lcsa.LCSA_OK
+    p4 = lcsa.problem(BASE.replace(kv_frames=4, q_frame0=0, q_frames=4))
+    assert lib.lcsa_stream_state_size(ctypes.byref(p4), 3, 7, ctypes.byref(n)) == lcsa.LCSA_ERR_UNSUPPORTED
+    st = lcsa.LcsaStream()
+    mem = ctypes.c_void_p(1 << 20)   # never dereferenced: no device work on these paths
+    assert lib.lcsa_stream_init(ctypes.byref(st), ctypes.byref(p), 3, 7, mem, 1024) == lcsa.LCSA_ERR_INVALID
+    assert b"needed" in lib.lcsa_last_error()
+    assert lib.lcsa_stream_init(ctypes.byref(st), ctypes.byref(p), 3, 7, ctypes.c_void_p((1 << 20) + 64),
+                                1 << 40) == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_stream_init(ctypes.byref(st), ctypes.byref(p), 3, 7, mem, 1 << 40) == lcsa.LCSA_OK
+    assert (st.held, st.pushed, st.wpos, st.cache_tblocks, st.ring_tblocks) == (0, 0, 0, 3, 7)
+    wp = lcsa.LcsaProblem()
+    assert lib.lcsa_stream_window(ctypes.byref(st), ctypes.byref(wp), None, None, None, None, None) \
+        == lcsa.LCSA_ERR_INVALID
+    zs = lcsa.LcsaStrides(0, 0, 0)
+    assert lib.lcsa_stream_push(ctypes.byref(st), None, zs, None, zs, None) == lcsa.LCSA_ERR_INVALID
+    assert (st.held, st.pushed, st.wpos) == (0, 0, 0)
+    # reserve below the end of the ring: no device work, the slot at wpos
+    ks = lcsa.LcsaStrides()
+    k = ctypes.c_void_p()
+    st.wpos = 4
+    st.held = 3
+    st.pushed = 9
+    assert lib.lcsa_stream_reserve(ctypes.byref(st), ctypes.byref(k), ctypes.byref(ks), None, None, None) \
+        == lcsa.LCSA_OK
+    assert k.value == (1 << 20) + 4 * blk and (ks.batch, ks.head, ks.token) == (Hh * 7 * 2 * hw * d, 7 * 2 * hw * d, d)
+    # window geometry from the host bookkeeping alone (no device work)
+    for pushed, held, wpos, kvf in [(1, 1, 1, 2), (2, 2, 2, 4), (3, 3, 3, 6), (9, 3, 4, 6), (8, 3, 7, 6)]:
+        st.pushed, st.held, st.wpos = pushed, held, wpos
+        k, v, kb = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+        vs = lcsa.LcsaStrides()
+        assert lib.lcsa_stream_window(ctypes.byref(st), ctypes.byref(wp), ctypes.byref(k), ctypes.byref(ks),
+                                      ctypes.byref(v), ctypes.byref(vs), ctypes.byref(kb)) == lcsa.LCSA_OK
+        assert (wp.kv_frames, wp.q_frame0, wp.q_frames) == (kvf, kvf - 2, 2)
+        assert k.value == (1 << 20) + (wpos - held) * blk
+        assert v.value == (1 << 20) + up(ring) + (wpos - held) * blk
+        assert kb.value == (1 << 20) + 2 * up(ring) + (0 if pushed % 2 else up(kbar))
+    st.wpos = 2   # just after a compacting reserve: no window until the push
+    assert lib.lcsa_stream_window(ctypes.byref(st), ctypes.byref(wp), None, None, None, None, None) \
+        == lcsa.LCSA_ERR_INVALID
+    assert b"compacted" in lib.lcsa_last_error()
+    st.wpos = 1   # fewer slots than that: rejected as an uninitialised state
+    assert lib.lcsa_stream_window(ctypes.byref(st), ctypes.byref(wp), None, None, None, None, None) \
+        == lcsa.LCSA_ERR_INVALID
+    assert b"not initialised" in lib.lcsa_last_error()

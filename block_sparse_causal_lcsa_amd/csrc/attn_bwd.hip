@@ -601,6 +601,8 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
   lcsa_status st = validate_problem(p, &g);
   if (st != LCSA_OK) return st;
   if (p->dtype != LCSA_BF16) return fail(LCSA_ERR_UNSUPPORTED, "lcsa_attn_bwd: only bf16 inputs are implemented");
+  if (p->grid_h % kBlkH || p->grid_w % kBlkW)
+    return fail(LCSA_ERR_UNSUPPORTED, "lcsa_attn_bwd: grids with partial edge blocks are not implemented");
   const int64_t hw = int64_t(p->grid_h) * p->grid_w;
   if ((st = check_tensor("q", q, qs, p, hw * p->q_frames)) != LCSA_OK) return st;
   if ((st = check_tensor("k", k, ks, p, hw * p->kv_frames)) != LCSA_OK) return st;

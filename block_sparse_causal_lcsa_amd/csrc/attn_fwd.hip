@@ -64,6 +64,26 @@ __device__ __forceinline__ int block_token(const Geom& g, int tr, int hb, int wb
   return ((kBlkT * tr + (r >> 6)) * g.H + kBlkH * hb + ((r >> 3) & 7)) * g.W + kBlkW * wb + (r & 7);
 }
 
+// Query row r (0..127) of block (hb, wb): whether it lies inside the grid, and the row to load in its
+// place when it does not (the nearest one inside, so every load stays in the tensor).
+__device__ __forceinline__ bool query_row_inside(const Geom& g, int hb, int wb, int r, int* r_load) {
+  const int rows = block_rows(g, hb), cols = block_cols(g, wb);
+  const int y = (r >> 3) & 7, x = r & 7;
+  *r_load = (r & 64) | ((y < rows ? y : rows - 1) << 3) | (x < cols ? x : cols - 1);
+  return y < rows && x < cols;
+}
+
+// Key tile of 64 keys (one frame of a block, tile row k = 8 * y + x): the score item v of 32-key
+// tile kt that a lane holds (S^T layout) is key kt*32 + 8*(v/4) + 4*hi + v%4. Keys outside the grid
+// of a partial block (rows x cols inside) get -inf, so they take no probability mass.
+__device__ __forceinline__ void mask_partial_tile(f32x16& s, int kt, int hi, int rows, int cols) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int y = kt * 4 + v / 4, x = 4 * hi + v % 4;
+    if (!(y < rows && x < cols)) s[v] = -INFINITY;
+  }
+}
+
 // Raw buffer resource over one (batch, head) slice of a token tensor: loads take a 32-bit lane
 // offset (VGPR) plus a 32-bit uniform offset (SGPR), so gathers cost no vector ALU work, and any
 // access past `bytes` returns zero instead of touching memory. The host guarantees spans < 4 GiB.
@@ -197,7 +217,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 
   const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
   const int qhb = qrem / g.Wb, qwb = qrem - (qrem / g.Wb) * g.Wb;
-  const int qtok = block_token(g, qtr, qhb, qwb, 32 * wave + l32);
+  int qrow_ld;
+  const bool q_in = query_row_inside(g, qhb, qwb, 32 * wave + l32, &qrow_ld);
+  const int qtok = block_token(g, qtr, qhb, qwb, qrow_ld);
 
   // B operand of S^T = K Q^T: lane holds Q[row l32][16*s + 8*hi + 0..7]
   bf16x8 qf[DS];
@@ -258,6 +280,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
       }
     }
+    {
+      // keys outside the grid in a partial block (last block row / column)
+      const int rem = jcur % g.bpt, hbk = rem / g.Wb, wbk = rem % g.Wb;
+      const int rows = block_rows(g, hbk), cols = block_cols(g, wbk);
+      if (rows < kBlkH || cols < kBlkW) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) mask_partial_tile(sacc[kt], kt & 1, hi, rows, cols);
+      }
+    }
     // online softmax in the log2 domain; this lane holds 64 of the row's 128 raw scores
     float mx = -INFINITY;
 #pragma unroll
@@ -308,6 +339,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (!q_in) return;  // a query row outside the grid (partial block) has no output
   T* ob = static_cast<T*>(a.o) + b * a.osb + h * a.osh + int64_t(qtok) * a.ost;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -431,7 +463,9 @@ __device__ __forceinline__ void wait_tiles(int n) {
   }
 }
 
-template <int D>
+// RAGGED: the grid is not a multiple of 8, so edge blocks are partial (masked keys, query rows
+// without output); the variant for whole blocks carries none of that.
+template <int D, bool RAGGED>
 __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int row_start, int nsel, int nsel_other, int lwave,
                                          uint16_t* kb0, uint16_t* kb1, uint16_t* vb0, uint16_t* vb1) {
   constexpr int DS = D / 16;
@@ -454,7 +488,9 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
   const uint16_t* vbp = static_cast<const uint16_t*>(a.v) + b * a.vsb + h * a.vsh;
   const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
   const int qhb = qrem / g.Wb, qwb = qrem - (qrem / g.Wb) * g.Wb;
-  const int qtok = block_token(g, qtr, qhb, qwb, 32 * lwave + l32);
+  int qrow_ld = 32 * lwave + l32;
+  const bool q_in = RAGGED ? query_row_inside(g, qhb, qwb, 32 * lwave + l32, &qrow_ld) : true;
+  const int qtok = block_token(g, qtr, qhb, qwb, qrow_ld);
 
   bf16x8 qf[DS];
   if (has) {
@@ -469,11 +505,13 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
   // scalar loads, which leave the vector-memory counter to the tile loads)
   const const_i32* sel = (const const_i32*)(a.col_idx) + int64_t(bh) * a.nnz + (has ? row_start : 0);
   const uint32_t hw = uint32_t(g.H) * uint32_t(g.W);
-  auto block_base = [&](int j, bool& ok) -> uint32_t {
+  // first token of kept block j; ok: j is a block; lim: 16 * rows + cols inside the grid (136: full)
+  auto block_base = [&](int j, bool& ok, int& lim) -> uint32_t {
     ok = j >= 0 && j < g.nkb;
     const uint32_t ju = ok ? uint32_t(j) : 0u;
     const uint32_t tr = fast_div(ju, a.div_bpt), rem = ju - tr * uint32_t(g.bpt);
     const uint32_t hb = fast_div(rem, a.div_wb), wb = rem - hb * uint32_t(g.Wb);
+    if constexpr (RAGGED) lim = 16 * block_rows(g, int(hb)) + block_cols(g, int(wb));
     return (kBlkT * tr * uint32_t(g.H) + kBlkH * hb) * uint32_t(g.W) + kBlkW * wb;
   };
 
@@ -488,11 +526,12 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
 
   // block n = current (ok_c, base_c), n + 1 (ok_n, base_n), entry of n + 2 (j_pref)
   bool ok_c = false, ok_n = false;
+  int lim_c = 136, lim_n = 136;
   uint32_t base_c = 0, base_n = 0;
   int j_pref = 0;
   if (t > 0) {
-    base_c = block_base(sel[0], ok_c);
-    if (nsel > 1) base_n = block_base(sel[1], ok_n);
+    base_c = block_base(sel[0], ok_c, lim_c);
+    if (nsel > 1) base_n = block_base(sel[1], ok_n, lim_n);
     if (nsel > 2) j_pref = sel[2];
     issue_tile<D, false>(krs, kb0, kst, base_c, g.W, lwave, lane);
     issue_tile<D, false>(krs, kb1, kst, base_c + hw, g.W, lwave, lane);
@@ -589,7 +628,13 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
       }
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
-  auto vphase = [&](bool ok) __attribute__((always_inline)) {
+  auto vphase = [&](bool ok, int lim) __attribute__((always_inline)) {
+    if constexpr (RAGGED) {
+      if (lim != 16 * kBlkH + kBlkW) {  // partial block at the grid edge (uniform branch)
+        mask_partial_tile(S[0], 0, hi, lim >> 4, lim & 15);
+        mask_partial_tile(S[1], 1, hi, lim >> 4, lim & 15);
+      }
+    }
     float ls = exps(ok ? -m_run : -INFINITY);
     if (__builtin_amdgcn_ballot_w64(!(ls <= kSumMax))) {
       const float mxs = ok ? tile_rowmax(S) * a.c : -INFINITY;
@@ -615,7 +660,7 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
     // ---- vector phase of m = 2n
     if constexpr (MORE) issue_tile<D, false>(krs, kb0, kst, base_n, g.W, lwave, lane);  // K(n+1, 0)
     issue_tile<D, true>(vrs, vb1, vst, base_c + hw, g.W, lwave, lane);                 // V(n, 1)
-    vphase(ok_c);
+    vphase(ok_c, lim_c);
     wait_tiles<LOADS>(MORE ? 2 : 1);  // K(n, 1) and V(n, 0) have landed
     phase_barrier();
     ++phase;
@@ -627,7 +672,7 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
       issue_tile<D, false>(krs, kb1, kst, base_n + hw, g.W, lwave, lane);  // K(n+1, 1)
       issue_tile<D, true>(vrs, vb0, vst, base_n, g.W, lwave, lane);        // V(n+1, 0)
     }
-    vphase(ok_c);
+    vphase(ok_c, lim_c);
     wait_tiles<LOADS>(MORE ? 2 : 0);  // K(n+1, 0) and V(n, 1) have landed
     phase_barrier();
     ++phase;
@@ -639,8 +684,9 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
     phase_barrier();
     ++phase;
     ok_c = ok_n;
+    lim_c = lim_n;
     base_c = base_n;
-    base_n = block_base(j_pref, ok_n);
+    base_n = block_base(j_pref, ok_n, lim_n);
     j_pref = jn;
   };
 
@@ -656,7 +702,7 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
     ++phase;
   }
 
-  if (!has) return;
+  if (!has || !q_in) return;  // no query block, or a query row outside the grid
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   uint16_t* ob = static_cast<uint16_t*>(a.o) + b * a.osb + h * a.osh + int64_t(qtok) * a.ost;
@@ -675,7 +721,7 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
   }
 }
 
-template <int D>
+template <int D, bool RAGGED>
 __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnArgs a) {
   constexpr int TE = Tile<D>::ELEMS;
   __shared__ __attribute__((aligned(16))) uint16_t k00[TE];
@@ -701,9 +747,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnArgs a) {
   const int G = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
   const int lwave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);
   if (G == 0)
-    pp_group<D>(a, 0, q0, r0, n0, n1, lwave, k00, k01, v00, v01);
+    pp_group<D, RAGGED>(a, 0, q0, r0, n0, n1, lwave, k00, k01, v00, v01);
   else
-    pp_group<D>(a, 1, q1 < nblocks ? q1 : -1, r1, n1, n0, lwave, k10, k11, v10, v11);
+    pp_group<D, RAGGED>(a, 1, q1 < nblocks ? q1 : -1, r1, n1, n0, lwave, k10, k11, v10, v11);
 }
 
 }  // namespace
@@ -753,8 +799,14 @@ extern "C" lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_
   (void)hipGetLastError();
   if (p->dtype == LCSA_BF16) {
     a.nwg = (a.nrows + 1) / 2;  // two query blocks per workgroup
-    if (p->head_dim == 128) attn_fwd_pp_kernel<128><<<a.nwg, 512, 0, s>>>(a);
-    else attn_fwd_pp_kernel<64><<<a.nwg, 512, 0, s>>>(a);
+    const bool ragged = (g.H % kBlkH) != 0 || (g.W % kBlkW) != 0;
+    if (p->head_dim == 128) {
+      if (ragged) attn_fwd_pp_kernel<128, true><<<a.nwg, 512, 0, s>>>(a);
+      else attn_fwd_pp_kernel<128, false><<<a.nwg, 512, 0, s>>>(a);
+    } else {
+      if (ragged) attn_fwd_pp_kernel<64, true><<<a.nwg, 512, 0, s>>>(a);
+      else attn_fwd_pp_kernel<64, false><<<a.nwg, 512, 0, s>>>(a);
+    }
   } else {
     if (p->head_dim == 128) attn_fwd_kernel<float, 128><<<a.nwg, 256, 0, s>>>(a);
     else attn_fwd_kernel<float, 64><<<a.nwg, 256, 0, s>>>(a);

@@ -23,7 +23,7 @@ constexpr int kBlkTokens = kBlkT * kBlkH * kBlkW;  // 128
 
 struct Geom {
   int32_t H, W;          // tokens per frame
-  int32_t Hb, Wb;        // blocks per frame
+  int32_t Hb, Wb;        // blocks per frame: ceil(H / 8), ceil(W / 8)
   int32_t bpt;           // blocks per temporal block = Hb * Wb
   int32_t nqb, nkb;      // query / key blocks per (batch, head)
   int32_t q_tb0;         // absolute temporal block of query block 0 (q_frame0 / 2)
@@ -91,6 +91,17 @@ inline FastDiv make_fastdiv(uint32_t d) {
 }
 
 LCSA_HD uint32_t fast_div(uint32_t n, const FastDiv& f) { return uint32_t((uint64_t(n) * f.m) >> f.k); }
+
+// Rows (1..8) of block row hb and columns (1..8) of block column wb that lie inside the grid: blocks
+// start at the spatial origin, so only the last block row and column can be partial.
+LCSA_HD int block_rows(const Geom& g, int hb) {
+  const int r = g.H - kBlkH * hb;
+  return r < kBlkH ? r : kBlkH;
+}
+LCSA_HD int block_cols(const Geom& g, int wb) {
+  const int c = g.W - kBlkW * wb;
+  return c < kBlkW ? c : kBlkW;
+}
 
 LCSA_HD int n_visible(const Geom& g, int i) {
   int h0, h1, w0, w1;

@@ -42,9 +42,6 @@ lcsa_status validate_problem(const lcsa_problem* p, Geom* g) {
     return fail(LCSA_ERR_UNSUPPORTED, "block %dx%dx%d: only 2x8x8 is implemented", p->blk_t, p->blk_h,
                 p->blk_w);
   if (p->grid_h < 1 || p->grid_w < 1) return fail(LCSA_ERR_INVALID, "grid must be positive");
-  if (p->grid_h % kBlkH || p->grid_w % kBlkW)
-    return fail(LCSA_ERR_UNSUPPORTED, "grid %dx%d is not a multiple of the 8x8 block", p->grid_h,
-                p->grid_w);
   if (p->kv_frames < 1 || p->q_frames < 1 || p->q_frame0 < 0)
     return fail(LCSA_ERR_INVALID, "frame counts must be positive and q_frame0 >= 0");
   if (p->q_frame0 + p->q_frames > p->kv_frames)
@@ -68,7 +65,9 @@ lcsa_status validate_problem(const lcsa_problem* p, Geom* g) {
 
   const int64_t hw = static_cast<int64_t>(p->grid_h) * p->grid_w;
   const int64_t nk_tok = hw * p->kv_frames;
-  const int64_t bpt = hw / (kBlkH * kBlkW);
+  // edge blocks of a grid that is not a multiple of 8 are partial (fewer rows or columns)
+  const int64_t hb_n = (p->grid_h + kBlkH - 1) / kBlkH, wb_n = (p->grid_w + kBlkW - 1) / kBlkW;
+  const int64_t bpt = hb_n * wb_n;
   const int64_t nkb = bpt * (p->kv_frames / kBlkT);
   // every kernel indexes blocks, rows and (batch, head) pairs with 32-bit integers
   if (nk_tok > (int64_t(1) << 30) || nkb * p->batch * p->heads > (int64_t(1) << 30))
@@ -76,8 +75,8 @@ lcsa_status validate_problem(const lcsa_problem* p, Geom* g) {
   if (g) {
     g->H = p->grid_h;
     g->W = p->grid_w;
-    g->Hb = p->grid_h / kBlkH;
-    g->Wb = p->grid_w / kBlkW;
+    g->Hb = static_cast<int32_t>(hb_n);
+    g->Wb = static_cast<int32_t>(wb_n);
     g->bpt = static_cast<int32_t>(bpt);
     g->nqb = static_cast<int32_t>(bpt * (p->q_frames / kBlkT));
     g->nkb = static_cast<int32_t>(nkb);

@@ -1,5 +1,6 @@
 // lcsa_pool: mean of every 2x8x8 token block of Q and K (FlashVSR summary, sec. 2.2: Q and K are
-// average-pooled per block into compact block features).
+// average-pooled per block into compact block features). Edge blocks of a grid that is not a
+// multiple of 8 are partial and averaged over the tokens they have.
 //
 // One workgroup (256 lanes) per (batch, head, block). A block is 16 rows of 8 consecutive tokens;
 // each lane owns one 16-byte chunk of a token row and walks the block's tokens with a fixed stride,
@@ -22,7 +23,8 @@ struct PoolTensor {
   int32_t out_rows, out_off;
 };
 
-template <typename T, int D>
+// RAGGED: the grid is not a multiple of 8 and edge blocks are partial.
+template <typename T, int D, bool RAGGED>
 __global__ __launch_bounds__(256) void pool_kernel(PoolTensor ta, PoolTensor tb, int heads, Geom g) {
   constexpr int EPC = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte chunk
   constexpr int CPT = D / EPC;                           // chunks per token row
@@ -41,6 +43,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolTensor ta, PoolTensor tb,
   const int tr = blk / g.bpt, rem = blk - (blk / g.bpt) * g.bpt;
   const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
   const T* base = static_cast<const T*>(t.x) + b * t.sb + h * t.sh;
+  // a block in the last block row / column of a grid that is not a multiple of 8 is partial
+  const int rows = RAGGED ? block_rows(g, hb) : kBlkH, cols = RAGGED ? block_cols(g, wb) : kBlkW;
 
   const int c = threadIdx.x % CPT;
   const int slot = threadIdx.x / CPT;
@@ -51,7 +55,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolTensor ta, PoolTensor tb,
     const int tok = slot + k * SLOTS;  // 0..127: (frame, row, col) = (tok/64, tok/8%8, tok%8)
     const int64_t n = (int64_t(kBlkT * tr + tok / 64) * g.H + kBlkH * hb + (tok / 8) % 8) * g.W +
                       kBlkW * wb + tok % 8;
-    raw[k] = *reinterpret_cast<const uint4*>(base + n * t.st + c * EPC);
+    const bool in = !RAGGED || ((tok / 8) % 8 < rows && tok % 8 < cols);
+    raw[k] = in ? *reinterpret_cast<const uint4*>(base + n * t.st + c * EPC) : make_uint4(0, 0, 0, 0);
   }
   double acc[EPC];
 #pragma unroll
@@ -77,14 +82,17 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolTensor ta, PoolTensor tb,
     double s = 0.0;
 #pragma unroll
     for (int k = 0; k < SLOTS; ++k) s += part[k][threadIdx.x];
+    // the exact fp64 sum over the block's tokens, divided once by their count (a power of two, 128,
+    // for a full block) and rounded once to fp32
     t.out[(int64_t(bh) * t.out_rows + t.out_off + blk) * D + threadIdx.x] =
-        static_cast<float>(s * (1.0 / kBlkTokens));
+        static_cast<float>(s / static_cast<double>(kBlkT * rows * cols));
   }
 }
 
 template <typename T, int D>
 void launch(const PoolTensor& a, const PoolTensor& b, int heads, const Geom& g, hipStream_t s) {
-  pool_kernel<T, D><<<a.wgs + b.wgs, 256, 0, s>>>(a, b, heads, g);
+  if (g.H % kBlkH || g.W % kBlkW) pool_kernel<T, D, true><<<a.wgs + b.wgs, 256, 0, s>>>(a, b, heads, g);
+  else pool_kernel<T, D, false><<<a.wgs + b.wgs, 256, 0, s>>>(a, b, heads, g);
 }
 
 }  // namespace

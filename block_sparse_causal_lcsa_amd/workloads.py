@@ -54,7 +54,8 @@ class Workload:
 
     @property
     def blocks_per_tblock(self) -> int:
-        return (self.grid_h // self.blk_h) * (self.grid_w // self.blk_w)
+        # a grid that is not a multiple of the block is cut from its origin; edge blocks are partial
+        return (-(-self.grid_h // self.blk_h)) * (-(-self.grid_w // self.blk_w))
 
     @property
     def nqb(self) -> int:
@@ -78,6 +79,11 @@ TINY = Workload("tiny_t4_16x16_h2_d64_f32", batch=1, heads=2, head_dim=64, grid_
 CHUNK_768 = Workload("chunk_768x1408_q2_kv6", batch=1, heads=12, head_dim=128, grid_h=48, grid_w=88,
                      kv_frames=6, q_frame0=4, q_frames=2, keep_ratio=RHO)
 
+# One 720x1280 streaming chunk: 45x80 latent tokens (16 px per token), so the last block row is
+# partial (5 of 8 token rows).
+HD_720 = Workload("hd_720x1280_q2_kv6", batch=1, heads=12, head_dim=128, grid_h=45, grid_w=80,
+                  kv_frames=6, q_frame0=4, q_frames=2, keep_ratio=RHO)
+
 # Full-clip parallel (training-style) pass: 26 latent frames, block-causal.
 CLIP_768 = Workload("clip_768x1408_26f", batch=1, heads=12, head_dim=128, grid_h=48, grid_w=88,
                     kv_frames=26, q_frame0=0, q_frames=26, keep_ratio=RHO)
@@ -97,5 +103,5 @@ def sweep(rho: float) -> Workload:
                     grid_w=88, kv_frames=8, q_frame0=0, q_frames=8, keep_ratio=rho)
 
 
-ALL = [TINY, CHUNK_768, CLIP_768, UHD_TRUNC, UHD_PRES] + [sweep(r) for r in SWEEP_RHOS]
+ALL = [TINY, CHUNK_768, CLIP_768, UHD_TRUNC, UHD_PRES, HD_720] + [sweep(r) for r in SWEEP_RHOS]
 BY_NAME = {w.name: w for w in ALL}

@@ -54,7 +54,8 @@ typedef enum { LCSA_WIN_NONE = 0, LCSA_WIN_TRUNCATED = 1, LCSA_WIN_PRESERVING = 
 
 typedef struct {
   int32_t batch, heads, head_dim;  /* head_dim in {64, 128} */
-  int32_t grid_h, grid_w;          /* latent tokens per frame; multiples of blk_h / blk_w */
+  int32_t grid_h, grid_w;          /* latent tokens per frame (>= 1). Blocks are cut from the origin;
+                                      when not a multiple of 8, the last block row / column is partial */
   int32_t kv_frames;               /* K/V hold latent frames [0, kv_frames) */
   int32_t q_frame0, q_frames;      /* Q holds latent frames [q_frame0, q_frame0 + q_frames) */
   int32_t blk_t, blk_h, blk_w;     /* block shape in tokens; only 2 x 8 x 8 is implemented */
@@ -82,7 +83,8 @@ lcsa_status lcsa_csr_layout(const lcsa_problem* p, int32_t* nqb, int32_t* nkb,
 /* Block mean pooling (sec. 2.2: average pooling of Q and K over each block).
  * q: [B, Hh, q_frames*H*W, d] (dtype), k: [B, Hh, kv_frames*H*W, d] (dtype).
  * q_pooled: [B, Hh, nqb, d] fp32 contiguous; k_pooled: [B, Hh, nkb, d] fp32 contiguous.
- * Each output is the mean of the block's 128 tokens, accumulated in fp64, rounded once to fp32.
+ * Each output is the mean of the block's 128 tokens (fewer in a partial edge block: the tokens
+ * inside the grid), accumulated in fp64, rounded once to fp32.
  * q (with q_pooled) or k (with k_pooled) may be NULL to pool only the other tensor. */
 lcsa_status lcsa_pool(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
                       lcsa_strides ks, float* q_pooled, float* k_pooled, void* stream);
@@ -101,7 +103,8 @@ lcsa_status lcsa_score_select(const lcsa_problem* p, const float* q_pooled, cons
 /* Exact attention over the kept blocks (sec. 2.2 "full attention inside the selected blocks").
  * For each query token of block i: O = softmax(scale * q K_S^T) V_S over all tokens of the blocks
  * S = col_idx[b, h, row_ptr[i]:row_ptr[i+1]] (no token mask inside a kept block; a kept block is
- * always fully visible under block causality and a block-granular window).
+ * always fully visible under block causality and a block-granular window). In a partial edge block
+ * only the tokens inside the grid exist: they alone are keys, and only they get O and lse.
  * q: [B, Hh, Nq, d]; k, v: [B, Hh, Nk, d]; o: [B, Hh, Nq, d], all of the problem's dtype.
  * lse: NULL, or device fp32 [B, Hh, Nq] contiguous: natural log of the softmax denominator.
  * Arithmetic: bf16 inputs as given (fp32 inputs are rounded to bf16 on load), bf16 MFMA with fp32
@@ -127,7 +130,8 @@ lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_strides qs,
  *   no initial contents required; it must not be shared by calls that overlap in time.
  * Arithmetic: bf16 MFMA with fp32 accumulation; P and dS rounded to bf16 for the dV, dK and dQ
  * products; Delta in fp32 from the bf16 O. Deterministic: no atomics on the gradients.
- * Only bf16 problems are implemented (LCSA_ERR_UNSUPPORTED otherwise). */
+ * Only bf16 problems with grids that are multiples of 8 are implemented (LCSA_ERR_UNSUPPORTED
+ * otherwise). */
 lcsa_status lcsa_attn_bwd_workspace_size(const lcsa_problem* p, size_t* bytes);
 lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
                           lcsa_strides ks, const void* v, lcsa_strides vs, const void* o,

@@ -29,6 +29,9 @@ The passages leave several steps open; the readings taken here (all stated in DE
      Preserving: a w_b-wide window slid inward at the edge, start = clamp(c - r, 0, N - w_b),
      so every query keeps w_b blocks per axis when the grid has that many.
   R7 the pooled feature is the arithmetic mean of the block's 128 tokens.
+  R9 a grid that is not a multiple of 8 is cut into blocks from its origin; the last block row and
+     column are partial. A partial block is pooled over the tokens it has, and attention over a
+     kept partial block covers only those tokens. Block counts are ceil(H/8) x ceil(W/8).
 Every function works in fp64 on exact copies of the kernel inputs.
 
 The backward (`attend_bwd`) is not described by the sources: it is the exact gradient of `attend`
@@ -52,7 +55,9 @@ WIN_NONE, WIN_TRUNCATED, WIN_PRESERVING = 0, 1, 2
 
 # ----------------------------------------------------------------------------------- geometry
 def _grid(p):
-    hb, wb = p.grid_h // BLK_H, p.grid_w // BLK_W
+    """Blocks per frame along h and w: the grid is cut from its origin, the last block row/column
+    may be partial (R9)."""
+    hb, wb = -(-p.grid_h // BLK_H), -(-p.grid_w // BLK_W)
     return hb, wb
 
 
@@ -124,20 +129,20 @@ def csr_row_ptr(p, vis=None):
 
 def block_tokens(p, blk, frame0):
     """Token indices (raster order n = (t*H + h)*W + w) of block (tb, hb, wb) in a tensor whose
-    first latent frame is `frame0`."""
+    first latent frame is `frame0`; only the tokens inside the H x W grid (R9)."""
     tb, hb, wb = blk
     H, W = p.grid_h, p.grid_w
     idx = []
     for t in range(tb * BLK_T, tb * BLK_T + BLK_T):
-        for h in range(hb * BLK_H, hb * BLK_H + BLK_H):
-            for w in range(wb * BLK_W, wb * BLK_W + BLK_W):
+        for h in range(hb * BLK_H, min(hb * BLK_H + BLK_H, H)):
+            for w in range(wb * BLK_W, min(wb * BLK_W + BLK_W, W)):
                 idx.append(((t - frame0) * H + h) * W + w)
     return np.array(idx, dtype=np.int64)
 
 
 # ---------------------------------------------------------------------------------- pooling
 def pool(p, x, which: str):
-    """Mean of each block's 128 tokens (R7). x: [B, heads, N, d] -> [B, heads, nblk, d] fp64."""
+    """Mean of each block's tokens (R7: 128, fewer in a partial edge block, R9). x: [B, heads, N, d] -> [B, heads, nblk, d] fp64."""
     x = np.asarray(x, dtype=np.float64)
     blocks, f0 = (query_blocks(p), p.q_frame0) if which == "q" else (key_blocks(p), 0)
     out = np.empty(x.shape[:2] + (len(blocks), x.shape[3]), dtype=np.float64)

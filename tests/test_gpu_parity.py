@@ -111,6 +111,34 @@ def test_edge_cases(w):
     report(w.name, full_check(w, 0, qblocks=qb))
 
 
+# Grids that are not multiples of 8: the last block row / column is partial (its tokens inside the
+# grid are pooled, attended to, and the only ones with outputs).
+RAGGED = [
+    W.Workload("ragged_21x37", 1, 2, 128, 21, 37, 4, 2, 2, keep_ratio=0.4),
+    W.Workload("ragged_13x10_d64_win_pres", 1, 2, 64, 13, 10, 4, 0, 4, win_mode=2, win_h=24, win_w=24,
+               keep_ratio=0.5),
+    W.Workload("ragged_19x27_win_trunc_b2", 2, 2, 128, 19, 27, 6, 2, 4, win_mode=1, win_h=24, win_w=24,
+               keep_ratio=0.4),
+    W.Workload("ragged_9x7_f32", 1, 2, 128, 9, 7, 4, 2, 2, dtype="f32", keep_ratio=0.5),
+    W.Workload("ragged_3x5_below_one_block", 1, 1, 128, 3, 5, 6, 4, 2, topk=2),
+]
+
+
+@pytest.mark.parametrize("w", RAGGED, ids=lambda w: w.name)
+def test_ragged_grids(w):
+    report(w.name, full_check(w, 0))
+
+
+def test_hd_720x1280_ragged():
+    """A 720x1280 chunk: 45x80 latent tokens, the last block row 5 tokens deep; sampled query blocks
+    include the whole last block row."""
+    w = W.HD_720
+    Wb = w.grid_w // 8
+    last_row = [w.nqb - Wb + x for x in range(0, Wb, 3)] + [w.nqb - 1]
+    qb = sorted(set(sample_blocks(w, 6)) | set(last_row))
+    report(w.name, full_check(w, 0, qblocks=qb, bh=[(0, h) for h in (0, 6, 11)]))
+
+
 def test_exact_ties_go_to_lower_index():
     """Constant K makes every score of a row equal: the K_i lowest visible indices must be kept."""
     w = W.Workload("ties", 1, 2, 128, 24, 32, 6, 2, 4, keep_ratio=0.25)

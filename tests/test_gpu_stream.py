@@ -83,6 +83,12 @@ def test_stream_small_f32_d64_window_cache2():
     run_stream(seq, 2, seed=1, oracle_chunks=(3,), in_place=(2,))
 
 
+def test_stream_ragged_grid():
+    """A 21x37 grid (partial last block row and column) streamed through a 2-block cache."""
+    seq = W.Workload("stream_21x37_t8", 1, 2, 128, 21, 37, 8, 0, 8, keep_ratio=0.4)
+    run_stream(seq, 2, seed=4, oracle_chunks=(2,), in_place=(1,))
+
+
 def test_stream_cache1():
     seq = W.Workload("stream_16x24_t6_c1", 1, 2, 128, 16, 24, 6, 0, 6, topk=2)
     run_stream(seq, 1, seed=2, oracle_chunks=(1,), in_place=(2,))

@@ -55,6 +55,8 @@ def random_problems(n, seed):
     out = []
     for _ in range(n):
         Hb, Wb = int(rng.integers(1, 9)), int(rng.integers(1, 12))
+        # every third problem has a ragged grid (partial last block row / column)
+        dh, dw = (int(rng.integers(0, 8)), int(rng.integers(0, 8))) if len(out) % 3 == 2 else (0, 0)
         kvf = 2 * int(rng.integers(1, 5))
         qf = 2 * int(rng.integers(1, kvf // 2 + 1))
         q0 = 2 * int(rng.integers(0, (kvf - qf) // 2 + 1))
@@ -62,7 +64,7 @@ def random_problems(n, seed):
         wb_h, wb_w = 2 * int(rng.integers(0, 5)) + 1, 2 * int(rng.integers(0, 5)) + 1
         topk = int(rng.integers(0, 6))
         rho = float(rng.choice([0.05, 0.136, 0.25, 1 / 3, 0.5, 0.77, 1.0]))
-        out.append(W.Workload("r", 1, 2, 64, 8 * Hb, 8 * Wb, kvf, q0, qf, win_mode=mode,
+        out.append(W.Workload("r", 1, 2, 64, 8 * Hb - dh, 8 * Wb - dw, kvf, q0, qf, win_mode=mode,
                               win_h=8 * wb_h if mode else 0, win_w=8 * wb_w if mode else 0,
                               topk=topk, keep_ratio=rho))
     return out
@@ -83,7 +85,7 @@ BASE = W.CHUNK_768
 @pytest.mark.parametrize("change,status", [
     (dict(head_dim=96), lcsa.LCSA_ERR_UNSUPPORTED),
     (dict(head_dim=0), lcsa.LCSA_ERR_UNSUPPORTED),
-    (dict(grid_w=84), lcsa.LCSA_ERR_UNSUPPORTED),
+    (dict(grid_w=0), lcsa.LCSA_ERR_INVALID),
     (dict(blk_h=4), lcsa.LCSA_ERR_UNSUPPORTED),
     (dict(q_frame0=3, q_frames=2), lcsa.LCSA_ERR_UNSUPPORTED),
     (dict(kv_frames=7), lcsa.LCSA_ERR_UNSUPPORTED),
@@ -177,6 +179,9 @@ def test_backward_rejections_on_host():
     pf = lcsa.problem(BASE.replace(dtype="f32"))
     assert call(prob=pf) == lcsa.LCSA_ERR_UNSUPPORTED
     assert b"bf16" in lib.lcsa_last_error()
+    pr = lcsa.problem(BASE.replace(grid_h=45))
+    assert call(prob=pr) == lcsa.LCSA_ERR_UNSUPPORTED
+    assert b"partial" in lib.lcsa_last_error()
 
 
 def test_stream_struct_layout_matches_header(tmp_path):

@@ -36,7 +36,7 @@ def token_block_map(p):
         t = np.arange(frame0, frame0 + frames)[:, None, None] // 2
         h = np.arange(p.grid_h)[None, :, None] // 8
         w = np.arange(p.grid_w)[None, None, :] // 8
-        Hb, Wb = p.grid_h // 8, p.grid_w // 8
+        Hb, Wb = (p.grid_h + 7) // 8, (p.grid_w + 7) // 8   # partial edge blocks (R9)
         return (((t - frame0 // 2) * Hb + h) * Wb + w).ravel()
     return blocks(p.q_frame0, p.q_frames), blocks(0, p.kv_frames)
 
@@ -50,9 +50,10 @@ def sdpa(p, q, k, v, mask):
 
 @pytest.mark.parametrize("mode", [O.WIN_NONE, O.WIN_TRUNCATED, O.WIN_PRESERVING])
 @pytest.mark.parametrize("q0,qf,kvf", [(0, 4, 4), (2, 2, 6)])
-def test_full_selection_is_dense_masked_attention(mode, q0, qf, kvf):
+@pytest.mark.parametrize("grid", [(40, 32), (37, 27)], ids=["grid40x32", "ragged37x27"])
+def test_full_selection_is_dense_masked_attention(mode, q0, qf, kvf, grid):
     kw = dict(win_mode=mode, win_h=24, win_w=24) if mode else {}
-    p = small(grid_h=40, grid_w=32, q_frame0=q0, q_frames=qf, kv_frames=kvf, **kw)
+    p = small(grid_h=grid[0], grid_w=grid[1], q_frame0=q0, q_frames=qf, kv_frames=kvf, **kw)
     q, k, v = rand_qkv(p)
     r = O.forward(p, q, k, v)
     qbl, kbl = token_block_map(p)

@@ -60,6 +60,22 @@ def test_pool_matches_reshape_mean():
     np.testing.assert_allclose(O.pool(p, x, "k"), r, rtol=0, atol=1e-14)
 
 
+def test_pool_ragged_matches_padded_nanmean():
+    """A 21 x 13 grid: edge blocks are 5 rows / 5 columns deep. Padding the grid to 24 x 16 with NaN
+    and taking nanmean over each 2x8x8 tile must give the oracle's partial-block means (R9)."""
+    p = small(grid_h=21, grid_w=13, kv_frames=4)
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((p.batch, p.heads, 4 * 21 * 13, p.head_dim))
+    pad = np.full((p.batch, p.heads, 4, 24, 16, p.head_dim), np.nan)
+    pad[:, :, :, :21, :13] = x.reshape(p.batch, p.heads, 4, 21, 13, p.head_dim)
+    r = np.nanmean(pad.reshape(p.batch, p.heads, 2, 2, 3, 8, 2, 8, p.head_dim), axis=(3, 5, 7))
+    r = r.reshape(p.batch, p.heads, 2 * 3 * 2, p.head_dim)
+    np.testing.assert_allclose(O.pool(p, x, "k"), r, rtol=0, atol=1e-14)
+    # token counts per block: 128 inside, 2*5*8, 2*8*5 and 2*5*5 at the edges
+    counts = [len(O.block_tokens(p, blk, 0)) for blk in O.key_blocks(p)[:6]]
+    assert counts == [128, 80, 128, 80, 80, 50]
+
+
 # ------------------------------------------------------------------------------ selection
 def brute_rank_select(s, cand, k):
     """Selected iff fewer than k candidates come before it in (score desc, index asc)."""

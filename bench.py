@@ -65,6 +65,10 @@ def main():
     ap.add_argument("--stream", type=int, default=0, metavar="CACHE",
                     help="time chunk-by-chunk streaming with a K/V cache of CACHE temporal blocks "
                          "(lcsa_stream_push + pool(q) + score_select + attn_fwd per chunk); prints its own JSON line")
+    ap.add_argument("--layer", type=int, default=0, metavar="CACHE",
+                    help="time a DiT self-attention layer with random weights around streaming LCSA "
+                         "(QKV GEMM, 3D RoPE, stream push, pool/select/attention, output GEMM) per chunk, "
+                         "cache of CACHE temporal blocks; prints its own JSON line with LCSA's share")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3 counter runs: warmup + `steps` steps, then one plain device copy "
                          "of 256 MiB (the byte-counter calibration kernel); prints a short line")
@@ -83,6 +87,9 @@ def main():
     w = W.BY_NAME[args.workload]
     if args.stream:
         stream_bench(args, w)
+        return
+    if args.layer:
+        layer_bench(args, w)
         return
     p = lcsa.problem(w)
     dev = torch.device("cuda:0")
@@ -342,6 +349,62 @@ def stream_bench(args, w):
         "attention_tflops_per_chunk": round(flop / (ms * 1e-3) / 1e12, 2),
     }
     print(json.dumps(res), flush=True)
+
+
+def layer_bench(args, w):
+    """Steady-state chunk time of DitLcsaLayer (random weights, C = heads * head_dim) at the workload's
+    frame size, with per-stage HIP-event times and LCSA's share (stream push + pool/select/attention)
+    of the layer."""
+    import numpy as np
+    import torch
+
+    from block_sparse_causal_lcsa_amd import lcsa
+    from block_sparse_causal_lcsa_amd.layer import DitLcsaLayer
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    chunk = w.replace(kv_frames=2, q_frame0=0, q_frames=2)
+    layer = DitLcsaLayer(lcsa.problem(chunk), args.layer, seed=0, device=dev)
+    N, C = 2 * w.grid_h * w.grid_w, w.heads * w.head_dim
+    g = torch.Generator(device="cpu").manual_seed(1)
+    xs = [torch.randn(w.batch, N, C, generator=g).to(torch.bfloat16).to(dev) for _ in range(4)]
+    c = 0
+    for _ in range(max(args.warmup, args.layer)):
+        layer.step(xs[c % 4])
+        c += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.step(xs[c % 4])
+        c += 1
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for e in evs:
+        _, res = layer.step(xs[c % 4], timing=e)
+        c += 1
+    torch.cuda.synchronize()
+    names = ["qkv_gemm", "rope_qkv", "stream_push", "pool_select_attn", "out_gemm"]
+    med = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    tot = float(np.median([e[0].elapsed_time(e[5]) for e in evs]))
+    lcsa_ms = med["stream_push"] + med["pool_select_attn"]
+    nnz = int(res["row_ptr"][-1])
+    gemm_flop = 2.0 * w.batch * N * C * 4 * C
+    res_out = {
+        "metric": "DiT attention layer ms per chunk with streaming LCSA (random weights), LCSA share",
+        "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic: x ~ N(0,1), weights ~ N(0, 1/C), bf16",
+        "config": {"workload": f"{w.name} as a DiT layer, cache {args.layer} temporal blocks", "heads": w.heads,
+                   "head_dim": w.head_dim, "model_dim": C, "tokens_per_chunk": N, "rope_dims": [44, 42, 42],
+                   "selected_pairs": w.batch * w.heads * nnz},
+        "stages_ms_median": {k: round(v, 4) for k, v in med.items()},
+        "layer_events_ms": round(tot, 4),
+        "lcsa_share": round(lcsa_ms / tot, 4),
+        "gemm_tflops": round(gemm_flop / ((med["qkv_gemm"] + med["out_gemm"]) * 1e-3) / 1e12, 1),
+        "rope_gbs": round(2 * w.batch * N * 3 * C * 2 / (med["rope_qkv"] * 1e-3) / 1e9, 1),
+    }
+    print(json.dumps(res_out), flush=True)
 
 
 def cpu_baseline(w, x, sample_blocks):

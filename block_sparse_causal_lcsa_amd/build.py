@@ -16,7 +16,7 @@ OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblcsa.so")
 ARCH = "gfx950"
 
-KERNELS = ["pool.hip", "score_select.hip", "attn_fwd.hip", "attn_bwd.hip", "stream.hip"]
+KERNELS = ["pool.hip", "score_select.hip", "attn_fwd.hip", "attn_bwd.hip", "stream.hip", "rope.hip"]
 HOST = ["lcsa_host.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 # Packed fp32 VALU ops are kept out of every device build.

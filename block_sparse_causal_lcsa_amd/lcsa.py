@@ -21,7 +21,7 @@ LCSA_BF16, LCSA_F32 = 0, 1
 EXPORTS = ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
            "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd",
            "lcsa_stream_state_size", "lcsa_stream_init", "lcsa_stream_reserve", "lcsa_stream_push",
-           "lcsa_stream_window",
+           "lcsa_stream_window", "lcsa_rope_qkv",
            "lcsa_status_string", "lcsa_last_error", "lcsa_version")
 
 
@@ -40,6 +40,11 @@ class LcsaStream(ctypes.Structure):
     _fields_ = [("chunk", LcsaProblem), ("cache_tblocks", ctypes.c_int32), ("ring_tblocks", ctypes.c_int32),
                 ("held", ctypes.c_int32), ("wpos", ctypes.c_int32), ("pushed", ctypes.c_int64),
                 ("mem", ctypes.c_void_p), ("mem_bytes", ctypes.c_size_t)]
+
+
+class LcsaRope(ctypes.Structure):
+    _fields_ = [("dim_t", ctypes.c_int32), ("dim_h", ctypes.c_int32), ("dim_w", ctypes.c_int32),
+                ("theta", ctypes.c_float)]
 
 
 class LcsaError(RuntimeError):
@@ -73,6 +78,8 @@ def load():
     lib.lcsa_attn_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.lcsa_attn_bwd.argtypes = [P, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, vp, vp, vp, vp,
                                   ctypes.c_size_t, vp]
+    lib.lcsa_rope_qkv.argtypes = [P, ctypes.POINTER(LcsaRope), vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_int32, vp, S, vp, S, vp, S, vp]
     SP = ctypes.POINTER(LcsaStream)
     lib.lcsa_stream_state_size.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.lcsa_stream_init.argtypes = [SP, P, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_size_t]
@@ -83,7 +90,7 @@ def load():
                                        ctypes.POINTER(S), ctypes.POINTER(vp)]
     for f in ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
               "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd", "lcsa_stream_state_size", "lcsa_stream_init",
-              "lcsa_stream_reserve", "lcsa_stream_push", "lcsa_stream_window"):
+              "lcsa_stream_reserve", "lcsa_stream_push", "lcsa_stream_window", "lcsa_rope_qkv"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lcsa_status_string.argtypes = [ctypes.c_int]
     lib.lcsa_status_string.restype = ctypes.c_char_p
@@ -332,8 +339,9 @@ class Stream:
                                                        (kbp.value - base) // 4)
         return p, k, v, kbar
 
-    def forward(self, q, stream=None):
-        """The newest chunk's attention: q [B, Hh, 2*H*W, d] are its query frames."""
+    def forward(self, q, o=None, stream=None):
+        """The newest chunk's attention: q [B, Hh, 2*H*W, d] are its query frames; o, if given, is
+        the output view (any strides the C ABI accepts, e.g. a [B, N, Hh, d] buffer permuted)."""
         torch = _torch()
         p, k, v, kbar = self.window()
         key = p.kv_frames
@@ -342,5 +350,28 @@ class Stream:
         row_ptr = self._rp[key]
         qp, _ = lcsa_pool(p, q, None, stream=stream)
         col = lcsa_score_select(p, qp, kbar, row_ptr, stream=stream)
-        o, lse = lcsa_attn_fwd(p, q, k, v, row_ptr, col, stream=stream)
+        o, lse = lcsa_attn_fwd(p, q, k, v, row_ptr, col, o=o, stream=stream)
         return dict(problem=p, q_pooled=qp, k_pooled=kbar, row_ptr=row_ptr, col_idx=col, o=o, lse=lse)
+
+
+# ---------------------------------------------------------------------------------- 3D RoPE
+def lcsa_rope_qkv(p: LcsaProblem, rope: LcsaRope, qkv, frame0: int, q=None, k=None, v=None, stream=None):
+    """qkv: bf16 [B, N, 3 * heads * head_dim] (rows [3][heads][d]) for latent frames
+    [frame0, frame0 + N / (H*W)) -> rope(q), rope(k), v as [B, heads, N, d] tensors (given ones are
+    written in place, e.g. the views of Stream.reserve())."""
+    torch = _torch()
+    hw = p.grid_h * p.grid_w
+    if qkv.dim() != 3 or qkv.dtype != torch.bfloat16 or qkv.stride(2) != 1 or qkv.shape[0] != p.batch \
+            or qkv.shape[2] != 3 * p.heads * p.head_dim or qkv.shape[1] % hw:
+        raise ValueError("qkv must be bf16 [B, frames*H*W, 3*heads*head_dim] with unit last stride")
+    n = qkv.shape[1]
+    outs = []
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is None:
+            t = torch.empty((p.batch, p.heads, n, p.head_dim), dtype=torch.bfloat16, device=qkv.device)
+        _check_token_tensor(name, t, p, n)
+        outs.append(t)
+    _check(load().lcsa_rope_qkv(ctypes.byref(p), ctypes.byref(rope), _ptr(qkv), qkv.stride(0), qkv.stride(1),
+                                frame0, n // hw, _ptr(outs[0]), _strides(outs[0]), _ptr(outs[1]),
+                                _strides(outs[1]), _ptr(outs[2]), _strides(outs[2]), _stream(stream)))
+    return tuple(outs)

@@ -194,6 +194,29 @@ lcsa_status lcsa_stream_push(lcsa_stream* s, const void* k_new, lcsa_strides ks,
 lcsa_status lcsa_stream_window(const lcsa_stream* s, lcsa_problem* window, const void** k, lcsa_strides* ks,
                                const void** v, lcsa_strides* vs, const float** k_pooled);
 
+/* 3D rotary position embedding and head split for a DiT attention layer feeding LCSA. The pages
+ * place LCSA in the self-attention of a Wan2.1 DiT (fmread summary, sec. 2.2 Stage 1) whose queries
+ * and keys carry rotary position embeddings over (time, height, width) (sec. 2.3 discusses their
+ * periodicity at high resolution); the projection and RoPE precede the pooling.
+ * Rotary dims: head_dim = dim_t + dim_h + dim_w (each even); the pairs (x[2i], x[2i+1]) of the
+ * first dim_t/2 pairs rotate by f * theta^(-2i/dim_t), the next dim_h/2 pairs by
+ * h * theta^(-2i'/dim_h), the last dim_w/2 pairs by w * theta^(-2i''/dim_w), where (f, h, w) is the
+ * token's absolute latent frame and spatial position. */
+typedef struct {
+  int32_t dim_t, dim_h, dim_w;
+  float theta;
+} lcsa_rope;
+
+/* qkv: bf16 device tensor of tokens of latent frames [frame0, frame0 + frames) of one chunk,
+ * token n (raster order within those frames) of batch b at qkv + b*qkv_batch + n*qkv_token,
+ * holding [3][heads][head_dim] (q, k, v), the layout a [tokens, 3*heads*head_dim] projection
+ * output has. Writes rope(q), rope(k) and v as [B, heads, frames*H*W, head_dim] bf16 with the given
+ * strides (for example into lcsa_stream_reserve's slot). Computes in fp32, rounds once to bf16.
+ * p supplies batch, heads, head_dim, grid and dtype (bf16 only); frames is even (>= 2). */
+lcsa_status lcsa_rope_qkv(const lcsa_problem* p, const lcsa_rope* rope, const void* qkv, int64_t qkv_batch,
+                          int64_t qkv_token, int32_t frame0, int32_t frames, void* q, lcsa_strides qs,
+                          void* k, lcsa_strides ks, void* v, lcsa_strides vs, void* stream);
+
 const char* lcsa_status_string(lcsa_status s);
 const char* lcsa_last_error(void);   /* thread-local detail of this thread's last non-OK return */
 int32_t lcsa_version(void);          /* major*10000 + minor*100 + patch */

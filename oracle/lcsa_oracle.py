@@ -29,6 +29,10 @@ The passages leave several steps open; the readings taken here (all stated in DE
      Preserving: a w_b-wide window slid inward at the edge, start = clamp(c - r, 0, N - w_b),
      so every query keeps w_b blocks per axis when the grid has that many.
   R7 the pooled feature is the arithmetic mean of the block's 128 tokens.
+  R10 (the attention layer around LCSA) Q and K carry a rotary position embedding over (time,
+     height, width): the head dim splits into three even groups, one per axis; adjacent dims form
+     the rotated pairs; frequencies theta^(-2j/dim_axis); positions are the absolute latent frame
+     and the token row and column. The pages only name the embedding (sec. 2.3).
   R9 a grid that is not a multiple of 8 is cut into blocks from its origin; the last block row and
      column are partial. A partial block is pooled over the tokens it has, and attention over a
      kept partial block covers only those tokens. Block counts are ceil(H/8) x ceil(W/8).
@@ -295,6 +299,29 @@ def stream_forward(p, q_seq, k_seq, v_seq, cache_tblocks: int, chunks=None):
         k = k_seq[:, :, first * tbt:(c + 1) * tbt]
         v = v_seq[:, :, first * tbt:(c + 1) * tbt]
         out[c] = forward(pw, q, k, v)
+    return out
+
+
+def rope_3d(p, x, frame0: int, dims, theta: float):
+    """3D rotary position embedding (R10) of x [B, heads, N, d] whose tokens are latent frames
+    frame0, frame0 + 1, ... of a grid_h x grid_w grid in raster order. dims = (dim_t, dim_h, dim_w),
+    summing to d: pair i = (x[2i], x[2i+1]) of the first dim_t/2 pairs turns by f * theta^(-2i/dim_t)
+    (f the absolute frame), the next dim_h/2 pairs by h * theta^(-2i'/dim_h), the last dim_w/2 by
+    w * theta^(-2i''/dim_w); a turn by a maps (x0, x1) to (x0 cos a - x1 sin a, x0 sin a + x1 cos a)."""
+    x = np.asarray(x, dtype=np.float64)
+    H, W = p.grid_h, p.grid_w
+    n = np.arange(x.shape[2])
+    pos = {"t": frame0 + n // (H * W), "h": (n % (H * W)) // W, "w": n % W}
+    angles = []
+    for axis, dim in zip("thw", dims):
+        for j in range(dim // 2):
+            angles.append(pos[axis] * float(theta) ** (-2.0 * j / dim))
+    ang = np.stack(angles, axis=1)                    # [N, d/2]
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
     return out
 
 

@@ -257,3 +257,42 @@ def test_stream_state_on_host():
     assert lib.lcsa_stream_window(ctypes.byref(st), ctypes.byref(wp), None, None, None, None, None) \
         == lcsa.LCSA_ERR_INVALID
     assert b"not initialised" in lib.lcsa_last_error()
+
+
+def test_rope_rejections_on_host():
+    lib = lcsa.load()
+    chunk = BASE.replace(kv_frames=2, q_frame0=0, q_frames=2)
+    p = lcsa.problem(chunk)
+    d = BASE.head_dim
+    hw = BASE.grid_h * BASE.grid_w
+    buf = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    st = lcsa.LcsaStrides(12 * 2 * hw * d, 2 * hw * d, d)
+    row = 3 * 12 * d
+
+    def call(rope, frames=2, qkv=buf, tok=row, prob=p):
+        r = ctypes.byref(rope) if rope is not None else None
+        return lib.lcsa_rope_qkv(ctypes.byref(prob), r, qkv, 2 * hw * row, tok, 0, frames, buf, st, buf, st, buf, st,
+                                 None)
+
+    assert call(None) == lcsa.LCSA_ERR_INVALID
+    assert call(lcsa.LcsaRope(44, 42, 40, 10000.0)) == lcsa.LCSA_ERR_INVALID       # sum != head_dim
+    assert call(lcsa.LcsaRope(43, 43, 42, 10000.0)) == lcsa.LCSA_ERR_INVALID       # odd dims
+    assert call(lcsa.LcsaRope(44, 42, 42, 1.0)) == lcsa.LCSA_ERR_INVALID           # theta
+    assert call(lcsa.LcsaRope(44, 42, 42, 10000.0), frames=3) == lcsa.LCSA_ERR_INVALID
+    assert call(lcsa.LcsaRope(44, 42, 42, 10000.0), tok=row - 8) == lcsa.LCSA_ERR_INVALID
+    assert call(lcsa.LcsaRope(44, 42, 42, 10000.0), qkv=ctypes.c_void_p((1 << 20) + 4)) == lcsa.LCSA_ERR_INVALID
+    pf = lcsa.problem(chunk.replace(dtype="f32"))
+    assert call(lcsa.LcsaRope(44, 42, 42, 10000.0), prob=pf) == lcsa.LCSA_ERR_UNSUPPORTED
+
+
+def test_rope_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "rlayout.c"
+    fields = [f[0] for f in lcsa.LcsaRope._fields_]
+    body = "".join(f'printf("%zu ", offsetof(lcsa_rope, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "lcsa.h"\n'
+                   f'int main(void){{ {body} printf("%zu\\n", sizeof(lcsa_rope)); return 0; }}\n')
+    exe = tmp_path / "rlayout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    assert got[:-1] == [getattr(lcsa.LcsaRope, f).offset for f in fields]
+    assert got[-1] == ctypes.sizeof(lcsa.LcsaRope)

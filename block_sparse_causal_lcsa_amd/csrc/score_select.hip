@@ -2,7 +2,7 @@
 // (FlashVSR summary, sec. 2.2: a coarse block-to-block attention map from the pooled features,
 // the Top-K most relevant block pairs are kept; sec. 2.3: the local spatial window).
 //
-// One workgroup (16 waves) per (batch, head, tile of 16 query blocks).
+// One workgroup (16 or 4 waves) per (batch, head, tile of 16 or 4 query blocks).
 //  1. Scores: s_ij = scale * <qbar_i, kbar_j> for the tile's 16 rows against every key block up to
 //     the last temporal block the tile can see, as fp64 MFMA 16x16x4 tiles (the pooled fp32
 //     features are widened exactly). Column tiles with no visible entry are skipped. Rows of 16
@@ -25,8 +25,9 @@ namespace {
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRows = 16;                 // query blocks per workgroup, one wave each
-constexpr int kThreads = 64 * kRows;
+// ROWS query blocks per workgroup, one wave each: 16 shares each loaded pooled-K tile among 16
+// rows; 4 gives four times the workgroups when a problem has too few rows to fill the chip.
+constexpr int kRowsWide = 16, kRowsNarrow = 4;
 constexpr int kMaxCols = 1248;            // key blocks one row can hold in LDS
 constexpr int kMaxSlots = (kMaxCols + 63) / 64;
 constexpr int kLdsPad = 2;
@@ -66,8 +67,8 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-template <int D, int SLOTS>
-__global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
+template <int D, int SLOTS, int kRows>
+__global__ __launch_bounds__(64 * kRows) void score_select_kernel(SelArgs a) {
   extern __shared__ double S[];  // [kRows][a.ld]
   const Geom& g = a.g;
   const int tiles = (g.nqb + kRows - 1) / kRows;
@@ -127,7 +128,8 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
     }
     // result item rr of lane (lr, lg) is D[row lg + 4*rr][col lr]
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) S[(lg + 4 * rr) * a.ld + j] = vis[rr] ? acc[rr] * a.scale : -INFINITY;
+    for (int rr = 0; rr < 4; ++rr)
+      if (lg + 4 * rr < kRows) S[(lg + 4 * rr) * a.ld + j] = vis[rr] ? acc[rr] * a.scale : -INFINITY;
   }
   __syncthreads();
 
@@ -217,8 +219,8 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(SelArgs a) {
 // size a row can need), not on every call, so that launches can be captured into a HIP graph.
 constexpr int kMaxDevices = 64;
 
-template <int D, int SLOTS>
-lcsa_status launch(const SelArgs& a, int wgs, size_t lds, hipStream_t s) {
+template <int D, int SLOTS, int kRows>
+lcsa_status launch(const SelArgs& a, const Geom& g, int bh, hipStream_t s) {
   static std::atomic<uint64_t> raised[kMaxDevices];
   int dev = 0;
   lcsa_status st = hip_status(hipGetDevice(&dev), "lcsa_score_select device");
@@ -226,14 +228,25 @@ lcsa_status launch(const SelArgs& a, int wgs, size_t lds, hipStream_t s) {
   if (dev < 0 || dev >= kMaxDevices) return fail(LCSA_ERR_UNSUPPORTED, "lcsa_score_select: device %d", dev);
   if (raised[dev].load(std::memory_order_acquire) == 0) {
     const size_t max_lds = size_t(kRows) * (((kMaxCols + 15) / 16) * 16 + kLdsPad) * sizeof(double);
-    st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<D, SLOTS>),
+    st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<D, SLOTS, kRows>),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(max_lds)),
                     "lcsa_score_select LDS size");
     if (st != LCSA_OK) return st;
     raised[dev].store(1, std::memory_order_release);
   }
-  score_select_kernel<D, SLOTS><<<wgs, kThreads, lds, s>>>(a);
+  const size_t lds = size_t(kRows) * a.ld * sizeof(double);
+  const int wgs = bh * ((g.nqb + kRows - 1) / kRows);
+  score_select_kernel<D, SLOTS, kRows><<<wgs, 64 * kRows, lds, s>>>(a);
   return LCSA_OK;
+}
+
+// Rows per workgroup: 16 unless that leaves fewer than 128 workgroups (half the CUs), then 4
+// (measured at the 768x1408 chunk, 60 -> 204 workgroups: 21 -> 14 us; at the 1536x2688 chunk,
+// with 192 workgroups of 16, the narrow form was slower: it reloads pooled K per 4 rows).
+template <int D, int SLOTS>
+lcsa_status launch_rows(const SelArgs& a, const Geom& g, int bh, hipStream_t s) {
+  if (bh * ((g.nqb + kRowsWide - 1) / kRowsWide) >= 128) return launch<D, SLOTS, kRowsWide>(a, g, bh, s);
+  return launch<D, SLOTS, kRowsNarrow>(a, g, bh, s);
 }
 
 }  // namespace
@@ -261,21 +274,20 @@ extern "C" lcsa_status lcsa_score_select(const lcsa_problem* p, const float* q_p
   SelArgs a{q_pooled, k_pooled, row_ptr, col_idx, scores_dbg, g, nnz, 0, static_cast<double>(p->scale)};
   a.ld = ((g.nkb + 15) / 16) * 16 + kLdsPad;
   if (a.ld < 128) a.ld = 128;  // a row also holds the 256 radix counters of its selection
-  const size_t lds = size_t(kRows) * a.ld * sizeof(double);
-  const int wgs = p->batch * p->heads * ((g.nqb + kRows - 1) / kRows);
+  const int bh = p->batch * p->heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const int slots = (g.nkb + 63) / 64;
   if (p->head_dim == 128) {
-    if (slots <= 4) st = launch<128, 4>(a, wgs, lds, s);
-    else if (slots <= 8) st = launch<128, 8>(a, wgs, lds, s);
-    else if (slots <= 16) st = launch<128, 16>(a, wgs, lds, s);
-    else st = launch<128, kMaxSlots>(a, wgs, lds, s);
+    if (slots <= 4) st = launch_rows<128, 4>(a, g, bh, s);
+    else if (slots <= 8) st = launch_rows<128, 8>(a, g, bh, s);
+    else if (slots <= 16) st = launch_rows<128, 16>(a, g, bh, s);
+    else st = launch_rows<128, kMaxSlots>(a, g, bh, s);
   } else {
-    if (slots <= 4) st = launch<64, 4>(a, wgs, lds, s);
-    else if (slots <= 8) st = launch<64, 8>(a, wgs, lds, s);
-    else if (slots <= 16) st = launch<64, 16>(a, wgs, lds, s);
-    else st = launch<64, kMaxSlots>(a, wgs, lds, s);
+    if (slots <= 4) st = launch_rows<64, 4>(a, g, bh, s);
+    else if (slots <= 8) st = launch_rows<64, 8>(a, g, bh, s);
+    else if (slots <= 16) st = launch_rows<64, 16>(a, g, bh, s);
+    else st = launch_rows<64, kMaxSlots>(a, g, bh, s);
   }
   if (st != LCSA_OK) return st;
   return hip_status(hipGetLastError(), "lcsa_score_select launch");

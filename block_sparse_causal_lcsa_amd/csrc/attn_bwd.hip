@@ -67,6 +67,21 @@ __device__ __forceinline__ int block_token(const Geom& g, int tr, int hb, int wb
   return ((kBlkT * tr + (r >> 6)) * g.H + kBlkH * hb + ((r >> 3) & 7)) * g.W + kBlkW * wb + (r & 7);
 }
 
+// Row r (0..127) of block (hb, wb): whether it lies inside the grid, and the row to read in its place
+// when it does not (the nearest one inside, so every access stays in the tensor).
+__device__ __forceinline__ bool row_inside(const Geom& g, int hb, int wb, int r, int* r_use) {
+  const int rows = block_rows(g, hb), cols = block_cols(g, wb);
+  const int y = (r >> 3) & 7, x = r & 7;
+  *r_use = (r & 64) | ((y < rows ? y : rows - 1) << 3) | (x < cols ? x : cols - 1);
+  return y < rows && x < cols;
+}
+
+// rows * 16 + cols inside the grid of block j (136 for a whole block).
+__device__ __forceinline__ int block_lim(const Geom& g, int j) {
+  const int rem = j % g.bpt;
+  return 16 * block_rows(g, rem / g.Wb) + block_cols(g, rem % g.Wb);
+}
+
 // First token of block j (frame 0), for a tensor whose first temporal block is temporal block 0.
 __device__ __forceinline__ uint32_t block_base(const Geom& g, int j) {
   const int tr = j / g.bpt, rem = j - (j / g.bpt) * g.bpt;
@@ -298,7 +313,9 @@ __global__ __launch_bounds__(1024) void csc_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------- dq
-template <int D>
+// RAGGED: the grid is not a multiple of 8; partial edge blocks mask their missing keys and query
+// rows (the whole-block variant carries none of it).
+template <int D, bool RAGGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(BwdArgs a) {
   constexpr int DS = D / 16, DT = D / 32;
   constexpr int TE = TileB<D>::ELEMS;
@@ -310,7 +327,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, hi = lane >> 5;
   const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
   const int qhb = qrem / g.Wb, qwb = qrem - (qrem / g.Wb) * g.Wb;
-  const int qtok = block_token(g, qtr, qhb, qwb, 32 * wave + l32);
+  int qrow = 32 * wave + l32;
+  const bool q_in = RAGGED ? row_inside(g, qhb, qwb, 32 * wave + l32, &qrow) : true;
+  const int qtok = block_token(g, qtr, qhb, qwb, qrow);
 
   bf16x8 qf[DS], gf[DS];  // B operands: this lane's query row, d = 16*s + 8*hi .. +8
   {
@@ -337,16 +356,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
   // sub-tile m = frame m%2 of entry m/2; invalid entries load block 0 and contribute nothing
-  auto base_of = [&](int m, bool& ok) -> uint32_t {
+  auto base_of = [&](int m, bool& ok, int& lim) -> uint32_t {
     const int j = sel[m >> 1];
     ok = j >= 0 && j < g.nkb;
+    if constexpr (RAGGED) lim = block_lim(g, ok ? j : 0);
     return block_base(g, ok ? j : 0) + uint32_t(m & 1) * hw;
   };
   // One 64-key sub-tile = two 32-key tiles t, one at a time: S^T = K Q^T and dP^T = V dO^T, the vector
   // step dS^T = P^T (dP^T - Delta), then dQ^T += K^T dS^T. At two waves per SIMD the other wave fills
   // the gaps; an explicit MFMA list with operands read ahead (as in the dK/dV kernel) needs more
   // registers than two waves leave and was slower.
-  auto step = [&](const uint16_t* Kt, const uint16_t* Vt, bool ok) __attribute__((always_inline)) {
+  auto step = [&](const uint16_t* Kt, const uint16_t* Vt, bool ok, int lim) __attribute__((always_inline)) {
     const float neg = ok ? -lse2 : -INFINITY;  // a skipped entry gives P = dS = 0
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -355,6 +375,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int s = 0; s < DS; ++s) {
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Kt, t, s), qf[s], st, 0, 0, 0);
         pt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Vt, t, s), gf[s], pt, 0, 0, 0);
+      }
+      if constexpr (RAGGED) {
+        if (lim != 16 * kBlkH + kBlkW) mask_partial_tile(st, t, hi, lim >> 4, lim & 15);  // keys outside the grid
       }
       f32x16 d;
 #pragma unroll
@@ -376,23 +399,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // per CU hide the rest of the load latency)
   const int total = 2 * nsel;
   bool ok_c = false, ok_n = false;
+  int lim_c = 136, lim_n = 136;
   if (total > 0) {
-    const uint32_t b0 = base_of(0, ok_n);
+    const uint32_t b0 = base_of(0, ok_n, lim_n);
     load_tile<D>(krs, kbuf, kst, b0, g.W);
     load_tile<D>(vrs, vbuf, vst, b0, g.W);
   }
   for (int m = 0; m < total; ++m) {
     ok_c = ok_n;
+    lim_c = lim_n;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     tile_barrier();
     if (m + 1 < total) {
-      const uint32_t bn = base_of(m + 1, ok_n);
+      const uint32_t bn = base_of(m + 1, ok_n, lim_n);
       load_tile<D>(krs, kbuf + ((m + 1) & 1) * TE, kst, bn, g.W);
       load_tile<D>(vrs, vbuf + ((m + 1) & 1) * TE, vst, bn, g.W);
     }
-    step(kbuf + (m & 1) * TE, vbuf + (m & 1) * TE, ok_c);
+    step(kbuf + (m & 1) * TE, vbuf + (m & 1) * TE, ok_c, lim_c);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (!q_in) return;  // a query row outside the grid (partial block) has no gradient
 
   float* out = a.dq + (int64_t(bh) * a.nq_tok + qtok) * D;
 #pragma unroll
@@ -407,7 +433,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ----------------------------------------------------------------------------------------- dkdv
-template <int D>
+template <int D, bool RAGGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv_kernel(BwdArgs a) {
   constexpr int DS = D / 16, DT = D / 32;
   constexpr int TE = TileB<D>::ELEMS;
@@ -422,7 +448,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, hi = lane >> 5;
   const int ktr = j / g.bpt, krem = j - (j / g.bpt) * g.bpt;
   const int khb = krem / g.Wb, kwb = krem - (krem / g.Wb) * g.Wb;
-  const int ktok = block_token(g, ktr, khb, kwb, 32 * wave + l32);
+  int krow = 32 * wave + l32;
+  const bool k_in = RAGGED ? row_inside(g, khb, kwb, 32 * wave + l32, &krow) : true;
+  const int ktok = block_token(g, ktr, khb, kwb, krow);
 
   bf16x8 kf[DS], vf[DS];  // B operands: this lane's key row
   {
@@ -479,7 +507,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // (group A), the vector step P = 2^(c S - lse2), dS = P (dP - Delta), and NB products
   // dV^T += dO^T P, dK^T += Q^T dS (group B), issued as one MFMA list (op_pos) whose LDS operands
   // are read kLook MFMAs ahead.
-  auto step = [&](const uint16_t* Qt, const uint16_t* Gt, const float* rl) __attribute__((always_inline)) {
+  auto step = [&](const uint16_t* Qt, const uint16_t* Gt, const float* rl, int lim) __attribute__((always_inline)) {
     // LEAD = 0: the vector step of tile 0 follows A(0) directly (other orders and read-ahead depths
     // from 4 to 8 measured within 3%)
     constexpr int NA = 2 * DS, NB = 4 * DT, LEAD = 0, MIX0 = NA + LEAD, MIXN = NA - LEAD + NB;
@@ -496,6 +524,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     // item v of tile t is query row t*32 + (v/4)*8 + 4*hi + v%4 of the sub-tile
     auto vec = [&](int t) __attribute__((always_inline)) {
+      if constexpr (RAGGED) {
+        if (lim != 16 * kBlkH + kBlkW) mask_partial_tile(sc[t], t, hi, lim >> 4, lim & 15);  // queries outside the grid
+      }
       f32x16 pv, ds;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -542,9 +573,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     tile_barrier();                                  // ... and for every wave; stage m - 1 is free
     if (m + NBUF - 1 < total) issue(m + NBUF - 1);
     const int sb = m % NBUF;
-    step(qbuf + sb * TE, gbuf + sb * TE, rlbuf + sb * 2 * kTok);
+    step(qbuf + sb * TE, gbuf + sb * TE, rlbuf + sb * 2 * kTok, RAGGED ? block_lim(g, rows[m >> 1]) : 136);
   }
 
+  if (!k_in) return;  // a key row outside the grid (partial block) has no gradient
   float* ok_ = a.dk + (int64_t(bh) * a.nk_tok + ktok) * D;
   float* ov_ = a.dv + (int64_t(bh) * a.nk_tok + ktok) * D;
 #pragma unroll
@@ -601,8 +633,6 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
   lcsa_status st = validate_problem(p, &g);
   if (st != LCSA_OK) return st;
   if (p->dtype != LCSA_BF16) return fail(LCSA_ERR_UNSUPPORTED, "lcsa_attn_bwd: only bf16 inputs are implemented");
-  if (p->grid_h % kBlkH || p->grid_w % kBlkW)
-    return fail(LCSA_ERR_UNSUPPORTED, "lcsa_attn_bwd: grids with partial edge blocks are not implemented");
   const int64_t hw = int64_t(p->grid_h) * p->grid_w;
   if ((st = check_tensor("q", q, qs, p, hw * p->q_frames)) != LCSA_OK) return st;
   if ((st = check_tensor("k", k, ks, p, hw * p->kv_frames)) != LCSA_OK) return st;
@@ -673,12 +703,23 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
     delta_kernel<64><<<int((ntok + 31) / 32), 256, 0, s>>>(a, ntok);
   }
   csc_kernel<<<bhn, 1024, 0, s>>>(a);
+  const bool ragged = (g.H % kBlkH) != 0 || (g.W % kBlkW) != 0;
   if (p->head_dim == 128) {
-    dq_kernel<128><<<bhn * g.nqb, 256, 0, s>>>(a);
-    dkdv_kernel<128><<<bhn * g.nkb, 256, 0, s>>>(a);
+    if (ragged) {
+      dq_kernel<128, true><<<bhn * g.nqb, 256, 0, s>>>(a);
+      dkdv_kernel<128, true><<<bhn * g.nkb, 256, 0, s>>>(a);
+    } else {
+      dq_kernel<128, false><<<bhn * g.nqb, 256, 0, s>>>(a);
+      dkdv_kernel<128, false><<<bhn * g.nkb, 256, 0, s>>>(a);
+    }
   } else {
-    dq_kernel<64><<<bhn * g.nqb, 256, 0, s>>>(a);
-    dkdv_kernel<64><<<bhn * g.nkb, 256, 0, s>>>(a);
+    if (ragged) {
+      dq_kernel<64, true><<<bhn * g.nqb, 256, 0, s>>>(a);
+      dkdv_kernel<64, true><<<bhn * g.nkb, 256, 0, s>>>(a);
+    } else {
+      dq_kernel<64, false><<<bhn * g.nqb, 256, 0, s>>>(a);
+      dkdv_kernel<64, false><<<bhn * g.nkb, 256, 0, s>>>(a);
+    }
   }
   return hip_status(hipGetLastError(), "lcsa_attn_bwd launch");
 }

@@ -73,17 +73,6 @@ __device__ __forceinline__ bool query_row_inside(const Geom& g, int hb, int wb, 
   return y < rows && x < cols;
 }
 
-// Key tile of 64 keys (one frame of a block, tile row k = 8 * y + x): the score item v of 32-key
-// tile kt that a lane holds (S^T layout) is key kt*32 + 8*(v/4) + 4*hi + v%4. Keys outside the grid
-// of a partial block (rows x cols inside) get -inf, so they take no probability mass.
-__device__ __forceinline__ void mask_partial_tile(f32x16& s, int kt, int hi, int rows, int cols) {
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int y = kt * 4 + v / 4, x = 4 * hi + v % 4;
-    if (!(y < rows && x < cols)) s[v] = -INFINITY;
-  }
-}
-
 // Raw buffer resource over one (batch, head) slice of a token tensor: loads take a 32-bit lane
 // offset (VGPR) plus a 32-bit uniform offset (SGPR), so gathers cost no vector ALU work, and any
 // access past `bytes` returns zero instead of touching memory. The host guarantees spans < 4 GiB.

@@ -8,6 +8,7 @@
 //   preserving: a w_b-wide window slid inward at the frame edge, start = clamp(c - r, 0, n - w_b).
 #pragma once
 
+#include <math.h>
 #include <stdint.h>
 
 #if defined(__HIPCC__)
@@ -101,6 +102,19 @@ LCSA_HD int block_rows(const Geom& g, int hb) {
 LCSA_HD int block_cols(const Geom& g, int wb) {
   const int c = g.W - kBlkW * wb;
   return c < kBlkW ? c : kBlkW;
+}
+
+// A 64-token tile is one frame of a block, tile row k = 8 * y + x. A 32x32 score accumulator of
+// the 32-row tile kt of such a tile (the MFMA result layout) holds, in item v of a lane with lane
+// half hi, tile row kt*32 + 8*(v/4) + 4*hi + v%4. Items whose token lies outside the grid of a
+// partial block (rows x cols inside) are set to -inf, so they take no probability mass.
+template <class V>
+LCSA_HD void mask_partial_tile(V& s, int kt, int hi, int rows, int cols) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int y = kt * 4 + v / 4, x = 4 * hi + v % 4;
+    if (!(y < rows && x < cols)) s[v] = -INFINITY;
+  }
 }
 
 LCSA_HD int n_visible(const Geom& g, int i) {

@@ -130,8 +130,8 @@ lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_strides qs,
  *   no initial contents required; it must not be shared by calls that overlap in time.
  * Arithmetic: bf16 MFMA with fp32 accumulation; P and dS rounded to bf16 for the dV, dK and dQ
  * products; Delta in fp32 from the bf16 O. Deterministic: no atomics on the gradients.
- * Only bf16 problems with grids that are multiples of 8 are implemented (LCSA_ERR_UNSUPPORTED
- * otherwise). */
+ * Partial edge blocks (grids that are not multiples of 8) hold only the tokens inside the grid, as in
+ * lcsa_attn_fwd. Only bf16 problems are implemented (LCSA_ERR_UNSUPPORTED otherwise). */
 lcsa_status lcsa_attn_bwd_workspace_size(const lcsa_problem* p, size_t* bytes);
 lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
                           lcsa_strides ks, const void* v, lcsa_strides vs, const void* o,

@@ -103,6 +103,11 @@ SMALL = [
     W.Workload("bwd_16x24_b2_pres_topk3", 2, 2, 128, 16, 24, 4, 0, 4, win_mode=2, win_h=8, win_w=24, topk=3),
     W.Workload("bwd_8x8_one_block", 1, 1, 64, 8, 8, 2, 0, 2, keep_ratio=1.0),
     W.Workload("bwd_16x40_topk1", 1, 2, 128, 16, 40, 6, 4, 2, topk=1),
+    # grids that are not multiples of 8: partial edge blocks
+    W.Workload("bwd_ragged_21x37", 1, 2, 128, 21, 37, 4, 2, 2, keep_ratio=0.4),
+    W.Workload("bwd_ragged_13x10_d64_pres", 1, 2, 64, 13, 10, 4, 0, 4, win_mode=2, win_h=24, win_w=24,
+               keep_ratio=0.5),
+    W.Workload("bwd_ragged_3x5", 1, 1, 128, 3, 5, 6, 4, 2, topk=2),
 ]
 
 

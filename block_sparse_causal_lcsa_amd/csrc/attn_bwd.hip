@@ -313,9 +313,13 @@ __global__ __launch_bounds__(1024) void csc_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------- dq
-// RAGGED: the grid is not a multiple of 8; partial edge blocks mask their missing keys and query
-// rows (the whole-block variant carries none of it).
-template <int D, bool RAGGED>
+// MASK: kMaskNone (whole blocks, block-granular windows: no token mask); kMaskRagged (the grid is
+// not a multiple of 8: partial edge blocks mask their missing keys and query rows); kMaskWindow
+// (token-granular window: per-token masks in blocks not seen whole by every query token; rows that
+// see no key have lse = -inf and get P = 0).
+constexpr int kMaskNone = 0, kMaskRagged = 1, kMaskWindow = 2;
+
+template <int D, int MASK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(BwdArgs a) {
   constexpr int DS = D / 16, DT = D / 32;
   constexpr int TE = TileB<D>::ELEMS;
@@ -328,8 +332,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
   const int qhb = qrem / g.Wb, qwb = qrem - (qrem / g.Wb) * g.Wb;
   int qrow = 32 * wave + l32;
-  const bool q_in = RAGGED ? row_inside(g, qhb, qwb, 32 * wave + l32, &qrow) : true;
+  const bool q_in = MASK != kMaskNone ? row_inside(g, qhb, qwb, 32 * wave + l32, &qrow) : true;
   const int qtok = block_token(g, qtr, qhb, qwb, qrow);
+  int lo_h = 0, hi_h = 0, lo_w = 0, hi_w = 0;  // this lane's query token window (kMaskWindow)
+  if constexpr (MASK == kMaskWindow) {
+    const bool pres = g.win_mode == kWinTokenPreserving;
+    tok_range(pres, kBlkH * qhb + ((qrow >> 3) & 7), g.H, g.wth, &lo_h, &hi_h);
+    tok_range(pres, kBlkW * qwb + (qrow & 7), g.W, g.wtw, &lo_w, &hi_w);
+  }
 
   bf16x8 qf[DS], gf[DS];  // B operands: this lane's query row, d = 16*s + 8*hi .. +8
   {
@@ -359,7 +369,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto base_of = [&](int m, bool& ok, int& lim) -> uint32_t {
     const int j = sel[m >> 1];
     ok = j >= 0 && j < g.nkb;
-    if constexpr (RAGGED) lim = block_lim(g, ok ? j : 0);
+    if constexpr (MASK == kMaskRagged) lim = block_lim(g, ok ? j : 0);
+    if constexpr (MASK == kMaskWindow) {
+      const int jj = ok ? j : 0, rem = jj % g.bpt, hb = rem / g.Wb, wb = rem % g.Wb;
+      lim = block_seen_whole(g, qhb, qwb, hb, wb) ? -1 : ((hb << 16) | wb);
+    }
     return block_base(g, ok ? j : 0) + uint32_t(m & 1) * hw;
   };
   // One 64-key sub-tile = two 32-key tiles t, one at a time: S^T = K Q^T and dP^T = V dO^T, the vector
@@ -367,7 +381,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the gaps; an explicit MFMA list with operands read ahead (as in the dK/dV kernel) needs more
   // registers than two waves leave and was slower.
   auto step = [&](const uint16_t* Kt, const uint16_t* Vt, bool ok, int lim) __attribute__((always_inline)) {
-    const float neg = ok ? -lse2 : -INFINITY;  // a skipped entry gives P = dS = 0
+    // a skipped entry, or a row that sees no key (lse = -inf), gives P = dS = 0
+    const float neg = ok && lse2 != -INFINITY ? -lse2 : -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16 st = f32x16{}, pt = f32x16{};
@@ -376,8 +391,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Kt, t, s), qf[s], st, 0, 0, 0);
         pt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Vt, t, s), gf[s], pt, 0, 0, 0);
       }
-      if constexpr (RAGGED) {
+      if constexpr (MASK == kMaskRagged) {
         if (lim != 16 * kBlkH + kBlkW) mask_partial_tile(st, t, hi, lim >> 4, lim & 15);  // keys outside the grid
+      }
+      if constexpr (MASK == kMaskWindow) {
+        if (lim >= 0)  // keys outside this query token's window
+          mask_window_tile(st, t, hi, kBlkH * (lim >> 16), kBlkW * (lim & 0xffff), lo_h, hi_h, lo_w, hi_w);
       }
       f32x16 d;
 #pragma unroll
@@ -433,7 +452,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ----------------------------------------------------------------------------------------- dkdv
-template <int D, bool RAGGED>
+template <int D, int MASK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv_kernel(BwdArgs a) {
   constexpr int DS = D / 16, DT = D / 32;
   constexpr int TE = TileB<D>::ELEMS;
@@ -449,8 +468,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int ktr = j / g.bpt, krem = j - (j / g.bpt) * g.bpt;
   const int khb = krem / g.Wb, kwb = krem - (krem / g.Wb) * g.Wb;
   int krow = 32 * wave + l32;
-  const bool k_in = RAGGED ? row_inside(g, khb, kwb, 32 * wave + l32, &krow) : true;
+  const bool k_in = MASK != kMaskNone ? row_inside(g, khb, kwb, 32 * wave + l32, &krow) : true;
   const int ktok = block_token(g, ktr, khb, kwb, krow);
+  const int hk = kBlkH * khb + ((krow >> 3) & 7), wk = kBlkW * kwb + (krow & 7);  // this lane's key token
 
   bf16x8 kf[DS], vf[DS];  // B operands: this lane's key row
   {
@@ -524,8 +544,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     // item v of tile t is query row t*32 + (v/4)*8 + 4*hi + v%4 of the sub-tile
     auto vec = [&](int t) __attribute__((always_inline)) {
-      if constexpr (RAGGED) {
+      if constexpr (MASK == kMaskRagged) {
         if (lim != 16 * kBlkH + kBlkW) mask_partial_tile(sc[t], t, hi, lim >> 4, lim & 15);  // queries outside the grid
+      }
+      if constexpr (MASK == kMaskWindow) {
+        if (lim >= 0)  // query tokens whose window misses this lane's key, or outside the grid
+          mask_window_tile_q(sc[t], t, hi, kBlkH * (lim >> 16), kBlkW * (lim & 0xffff), hk, wk, g);
       }
       f32x16 pv, ds;
 #pragma unroll
@@ -537,7 +561,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = 4 * g4 + e;
-          pv[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.c, -lv[e]));
+          // a query row that sees no key (lse = -inf) gets P = 0
+          const float nl = MASK == kMaskWindow && lv[e] == -INFINITY ? -INFINITY : -lv[e];
+          pv[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.c, nl));
           ds[v] = pv[v] * (dp[t][v] - dv4[e]);
         }
       }
@@ -573,7 +599,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     tile_barrier();                                  // ... and for every wave; stage m - 1 is free
     if (m + NBUF - 1 < total) issue(m + NBUF - 1);
     const int sb = m % NBUF;
-    step(qbuf + sb * TE, gbuf + sb * TE, rlbuf + sb * 2 * kTok, RAGGED ? block_lim(g, rows[m >> 1]) : 136);
+    int lim = 136;
+    if constexpr (MASK == kMaskRagged) lim = block_lim(g, rows[m >> 1]);
+    if constexpr (MASK == kMaskWindow) {
+      const int qi = rows[m >> 1], rem = qi % g.bpt, qhb = rem / g.Wb, qwb = rem % g.Wb;
+      lim = block_seen_whole(g, qhb, qwb, khb, kwb) && block_rows(g, qhb) == kBlkH && block_cols(g, qwb) == kBlkW
+                ? -1 : ((qhb << 16) | qwb);
+    }
+    step(qbuf + sb * TE, gbuf + sb * TE, rlbuf + sb * 2 * kTok, lim);
   }
 
   if (!k_in) return;  // a key row outside the grid (partial block) has no gradient
@@ -704,21 +737,28 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
   }
   csc_kernel<<<bhn, 1024, 0, s>>>(a);
   const bool ragged = (g.H % kBlkH) != 0 || (g.W % kBlkW) != 0;
+  const int mask = token_window(g) ? kMaskWindow : (ragged ? kMaskRagged : kMaskNone);
   if (p->head_dim == 128) {
-    if (ragged) {
-      dq_kernel<128, true><<<bhn * g.nqb, 256, 0, s>>>(a);
-      dkdv_kernel<128, true><<<bhn * g.nkb, 256, 0, s>>>(a);
+    if (mask == kMaskWindow) {
+      dq_kernel<128, kMaskWindow><<<bhn * g.nqb, 256, 0, s>>>(a);
+      dkdv_kernel<128, kMaskWindow><<<bhn * g.nkb, 256, 0, s>>>(a);
+    } else if (mask == kMaskRagged) {
+      dq_kernel<128, kMaskRagged><<<bhn * g.nqb, 256, 0, s>>>(a);
+      dkdv_kernel<128, kMaskRagged><<<bhn * g.nkb, 256, 0, s>>>(a);
     } else {
-      dq_kernel<128, false><<<bhn * g.nqb, 256, 0, s>>>(a);
-      dkdv_kernel<128, false><<<bhn * g.nkb, 256, 0, s>>>(a);
+      dq_kernel<128, kMaskNone><<<bhn * g.nqb, 256, 0, s>>>(a);
+      dkdv_kernel<128, kMaskNone><<<bhn * g.nkb, 256, 0, s>>>(a);
     }
   } else {
-    if (ragged) {
-      dq_kernel<64, true><<<bhn * g.nqb, 256, 0, s>>>(a);
-      dkdv_kernel<64, true><<<bhn * g.nkb, 256, 0, s>>>(a);
+    if (mask == kMaskWindow) {
+      dq_kernel<64, kMaskWindow><<<bhn * g.nqb, 256, 0, s>>>(a);
+      dkdv_kernel<64, kMaskWindow><<<bhn * g.nkb, 256, 0, s>>>(a);
+    } else if (mask == kMaskRagged) {
+      dq_kernel<64, kMaskRagged><<<bhn * g.nqb, 256, 0, s>>>(a);
+      dkdv_kernel<64, kMaskRagged><<<bhn * g.nkb, 256, 0, s>>>(a);
     } else {
-      dq_kernel<64, false><<<bhn * g.nqb, 256, 0, s>>>(a);
-      dkdv_kernel<64, false><<<bhn * g.nkb, 256, 0, s>>>(a);
+      dq_kernel<64, kMaskNone><<<bhn * g.nqb, 256, 0, s>>>(a);
+      dkdv_kernel<64, kMaskNone><<<bhn * g.nkb, 256, 0, s>>>(a);
     }
   }
   return hip_status(hipGetLastError(), "lcsa_attn_bwd launch");

@@ -209,6 +209,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   int qrow_ld;
   const bool q_in = query_row_inside(g, qhb, qwb, 32 * wave + l32, &qrow_ld);
   const int qtok = block_token(g, qtr, qhb, qwb, qrow_ld);
+  // token-granular window of this lane's query token (rows [lo_h, hi_h], columns [lo_w, hi_w])
+  const bool tokwin = token_window(g);
+  int lo_h = 0, hi_h = 0, lo_w = 0, hi_w = 0;
+  if (tokwin) {
+    const bool pres = g.win_mode == kWinTokenPreserving;
+    tok_range(pres, kBlkH * qhb + ((qrow_ld >> 3) & 7), g.H, g.wth, &lo_h, &hi_h);
+    tok_range(pres, kBlkW * qwb + (qrow_ld & 7), g.W, g.wtw, &lo_w, &hi_w);
+  }
 
   // B operand of S^T = K Q^T: lane holds Q[row l32][16*s + 8*hi + 0..7]
   bf16x8 qf[DS];
@@ -270,12 +278,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       }
     }
     {
-      // keys outside the grid in a partial block (last block row / column)
       const int rem = jcur % g.bpt, hbk = rem / g.Wb, wbk = rem % g.Wb;
-      const int rows = block_rows(g, hbk), cols = block_cols(g, wbk);
-      if (rows < kBlkH || cols < kBlkW) {
+      if (tokwin) {
+        // keys outside this query token's window (which also excludes tokens past the grid edge)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) mask_partial_tile(sacc[kt], kt & 1, hi, rows, cols);
+        for (int kt = 0; kt < 4; ++kt)
+          mask_window_tile(sacc[kt], kt & 1, hi, kBlkH * hbk, kBlkW * wbk, lo_h, hi_h, lo_w, hi_w);
+      } else {
+        // keys outside the grid in a partial block (last block row / column)
+        const int rows = block_rows(g, hbk), cols = block_cols(g, wbk);
+        if (rows < kBlkH || cols < kBlkW) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) mask_partial_tile(sacc[kt], kt & 1, hi, rows, cols);
+        }
       }
     }
     // online softmax in the log2 domain; this lane holds 64 of the row's 128 raw scores
@@ -287,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     mx = ok ? fmaxf(mx, __shfl_xor(mx, 32)) * a.c : -INFINITY;  // c > 0, so max(c s) = c max(s)
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyMax)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -295,7 +310,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
     }
-    const float neg_m = ok ? -m_run : -INFINITY;  // a skipped entry gives P = exp2(-inf) = 0
+    // a skipped entry, or a row that has seen no key yet, gives P = exp2(-inf) = 0
+    const float neg_m = ok && m_run != -INFINITY ? -m_run : -INFINITY;
     float ls = 0.f;
     bf16x8 pf[4][2];
 #pragma unroll
@@ -452,9 +468,13 @@ __device__ __forceinline__ void wait_tiles(int n) {
   }
 }
 
-// RAGGED: the grid is not a multiple of 8, so edge blocks are partial (masked keys, query rows
-// without output); the variant for whole blocks carries none of that.
-template <int D, bool RAGGED>
+// MASK: kMaskNone for whole blocks and a block-granular window (no token mask at all);
+// kMaskRagged when the grid is not a multiple of 8 (partial edge blocks: masked keys, query rows
+// without output); kMaskWindow for a token-granular window (per-token masks in the blocks that are
+// not wholly inside every query token's window; also covers partial blocks).
+constexpr int kMaskNone = 0, kMaskRagged = 1, kMaskWindow = 2;
+
+template <int D, int MASK>
 __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int row_start, int nsel, int nsel_other, int lwave,
                                          uint16_t* kb0, uint16_t* kb1, uint16_t* vb0, uint16_t* vb1) {
   constexpr int DS = D / 16;
@@ -478,8 +498,21 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
   const int qtr = i / g.bpt, qrem = i - (i / g.bpt) * g.bpt;
   const int qhb = qrem / g.Wb, qwb = qrem - (qrem / g.Wb) * g.Wb;
   int qrow_ld = 32 * lwave + l32;
-  const bool q_in = RAGGED ? query_row_inside(g, qhb, qwb, 32 * lwave + l32, &qrow_ld) : true;
+  const bool q_in = MASK != kMaskNone ? query_row_inside(g, qhb, qwb, 32 * lwave + l32, &qrow_ld) : true;
   const int qtok = block_token(g, qtr, qhb, qwb, qrow_ld);
+  // token-granular window: this lane's query token sees rows [lo_h, hi_h], columns [lo_w, hi_w]; a key
+  // block inside [lo_max, hi_min] on both axes is seen whole by every token of the query block
+  int lo_h = 0, hi_h = 0, lo_w = 0, hi_w = 0, lo_max_h = 0, hi_min_h = 0, lo_max_w = 0, hi_min_w = 0;
+  if constexpr (MASK == kMaskWindow) {
+    const bool pres = g.win_mode == kWinTokenPreserving;
+    tok_range(pres, kBlkH * qhb + ((qrow_ld >> 3) & 7), g.H, g.wth, &lo_h, &hi_h);
+    tok_range(pres, kBlkW * qwb + (qrow_ld & 7), g.W, g.wtw, &lo_w, &hi_w);
+    int t0, t1;
+    tok_range(pres, kBlkH * qhb + block_rows(g, qhb) - 1, g.H, g.wth, &lo_max_h, &t1);
+    tok_range(pres, kBlkH * qhb, g.H, g.wth, &t0, &hi_min_h);
+    tok_range(pres, kBlkW * qwb + block_cols(g, qwb) - 1, g.W, g.wtw, &lo_max_w, &t1);
+    tok_range(pres, kBlkW * qwb, g.W, g.wtw, &t0, &hi_min_w);
+  }
 
   bf16x8 qf[DS];
   if (has) {
@@ -500,7 +533,12 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
     const uint32_t ju = ok ? uint32_t(j) : 0u;
     const uint32_t tr = fast_div(ju, a.div_bpt), rem = ju - tr * uint32_t(g.bpt);
     const uint32_t hb = fast_div(rem, a.div_wb), wb = rem - hb * uint32_t(g.Wb);
-    if constexpr (RAGGED) lim = 16 * block_rows(g, int(hb)) + block_cols(g, int(wb));
+    if constexpr (MASK == kMaskRagged) lim = 16 * block_rows(g, int(hb)) + block_cols(g, int(wb));
+    if constexpr (MASK == kMaskWindow) {
+      const int h0 = kBlkH * int(hb), w0 = kBlkW * int(wb);
+      const bool whole = h0 >= lo_max_h && h0 + kBlkH - 1 <= hi_min_h && w0 >= lo_max_w && w0 + kBlkW - 1 <= hi_min_w;
+      lim = whole ? -1 : ((int(hb) << 16) | int(wb));
+    }
     return (kBlkT * tr * uint32_t(g.H) + kBlkH * hb) * uint32_t(g.W) + kBlkW * wb;
   };
 
@@ -618,26 +656,50 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
   auto vphase = [&](bool ok, int lim) __attribute__((always_inline)) {
-    if constexpr (RAGGED) {
+    if constexpr (MASK == kMaskRagged) {
       if (lim != 16 * kBlkH + kBlkW) {  // partial block at the grid edge (uniform branch)
         mask_partial_tile(S[0], 0, hi, lim >> 4, lim & 15);
         mask_partial_tile(S[1], 1, hi, lim >> 4, lim & 15);
       }
     }
-    float ls = exps(ok ? -m_run : -INFINITY);
-    if (__builtin_amdgcn_ballot_w64(!(ls <= kSumMax))) {
-      const float mxs = ok ? tile_rowmax(S) * a.c : -INFINITY;
-      const float m_new = fmaxf(m_run, mxs);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
-      m_run = m_new;
-      l_run *= alpha;
+    if constexpr (MASK == kMaskWindow) {
+      if (lim >= 0) {  // a block not seen whole by every query token (uniform branch)
+        const int h0 = kBlkH * (lim >> 16), w0 = kBlkW * (lim & 0xffff);
+        mask_window_tile(S[0], 0, hi, h0, w0, lo_h, hi_h, lo_w, hi_w);
+        mask_window_tile(S[1], 1, hi, h0, w0, lo_h, hi_h, lo_w, hi_w);
+      }
+      // a row may see no key yet: its running maximum stays -inf and its probabilities 0, and every
+      // sub-block refreshes it until it sees one
+      float ls = exps(ok && m_run != -INFINITY ? -m_run : -INFINITY);
+      if (__builtin_amdgcn_ballot_w64(!(ls <= kSumMax) || (ok && m_run == -INFINITY))) {
+        const float mxs = ok ? tile_rowmax(S) * a.c : -INFINITY;
+        const float m_new = fmaxf(m_run, mxs);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
-      ls = exps(ok ? -m_run : -INFINITY);
+          for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+        ls = exps(ok && m_run != -INFINITY ? -m_run : -INFINITY);
+      }
+      l_run += ls;
+    } else {
+      float ls = exps(ok ? -m_run : -INFINITY);
+      if (__builtin_amdgcn_ballot_w64(!(ls <= kSumMax))) {
+        const float mxs = ok ? tile_rowmax(S) * a.c : -INFINITY;
+        const float m_new = fmaxf(m_run, mxs);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+        ls = exps(ok ? -m_run : -INFINITY);
+      }
+      l_run += ls;
     }
-    l_run += ls;
   };
 
   using Yes = std::integral_constant<bool, true>;
@@ -710,7 +772,7 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
   }
 }
 
-template <int D, bool RAGGED>
+template <int D, int MASK>
 __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnArgs a) {
   constexpr int TE = Tile<D>::ELEMS;
   __shared__ __attribute__((aligned(16))) uint16_t k00[TE];
@@ -736,9 +798,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnArgs a) {
   const int G = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
   const int lwave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);
   if (G == 0)
-    pp_group<D, RAGGED>(a, 0, q0, r0, n0, n1, lwave, k00, k01, v00, v01);
+    pp_group<D, MASK>(a, 0, q0, r0, n0, n1, lwave, k00, k01, v00, v01);
   else
-    pp_group<D, RAGGED>(a, 1, q1 < nblocks ? q1 : -1, r1, n1, n0, lwave, k10, k11, v10, v11);
+    pp_group<D, MASK>(a, 1, q1 < nblocks ? q1 : -1, r1, n1, n0, lwave, k10, k11, v10, v11);
 }
 
 }  // namespace
@@ -789,12 +851,15 @@ extern "C" lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_
   if (p->dtype == LCSA_BF16) {
     a.nwg = (a.nrows + 1) / 2;  // two query blocks per workgroup
     const bool ragged = (g.H % kBlkH) != 0 || (g.W % kBlkW) != 0;
+    const int mask = token_window(g) ? kMaskWindow : (ragged ? kMaskRagged : kMaskNone);
     if (p->head_dim == 128) {
-      if (ragged) attn_fwd_pp_kernel<128, true><<<a.nwg, 512, 0, s>>>(a);
-      else attn_fwd_pp_kernel<128, false><<<a.nwg, 512, 0, s>>>(a);
+      if (mask == kMaskWindow) attn_fwd_pp_kernel<128, kMaskWindow><<<a.nwg, 512, 0, s>>>(a);
+      else if (mask == kMaskRagged) attn_fwd_pp_kernel<128, kMaskRagged><<<a.nwg, 512, 0, s>>>(a);
+      else attn_fwd_pp_kernel<128, kMaskNone><<<a.nwg, 512, 0, s>>>(a);
     } else {
-      if (ragged) attn_fwd_pp_kernel<64, true><<<a.nwg, 512, 0, s>>>(a);
-      else attn_fwd_pp_kernel<64, false><<<a.nwg, 512, 0, s>>>(a);
+      if (mask == kMaskWindow) attn_fwd_pp_kernel<64, kMaskWindow><<<a.nwg, 512, 0, s>>>(a);
+      else if (mask == kMaskRagged) attn_fwd_pp_kernel<64, kMaskRagged><<<a.nwg, 512, 0, s>>>(a);
+      else attn_fwd_pp_kernel<64, kMaskNone><<<a.nwg, 512, 0, s>>>(a);
     }
   } else {
     if (p->head_dim == 128) attn_fwd_kernel<float, 128><<<a.nwg, 256, 0, s>>>(a);

@@ -28,9 +28,36 @@ struct Geom {
   int32_t bpt;           // blocks per temporal block = Hb * Wb
   int32_t nqb, nkb;      // query / key blocks per (batch, head)
   int32_t q_tb0;         // absolute temporal block of query block 0 (q_frame0 / 2)
-  int32_t win_mode;      // 0 none, 1 truncated, 2 preserving
-  int32_t wbh, wbw;      // window width in blocks per axis (odd), when win_mode != 0
+  int32_t win_mode;      // 0 none, 1 / 2 block-granular truncated / preserving, 3 / 4 token-granular
+  int32_t wbh, wbw;      // window width in blocks per axis (odd), modes 1 and 2
+  int32_t wth, wtw;      // window width in tokens per axis, modes 3 and 4
 };
+
+constexpr int kWinTokenTruncated = 3, kWinTokenPreserving = 4;
+
+LCSA_HD bool token_window(const Geom& g) { return g.win_mode >= kWinTokenTruncated; }
+
+// Token-granular window along an axis of n tokens: the w tokens starting at c - (w - 1) / 2 (the
+// query's own position is inside; an even w has one more token after c than before), cut to [0, n)
+// (truncated) or shifted inside (preserving; the whole axis when n <= w). Inclusive [lo, hi]; lo and
+// hi never decrease as c grows.
+LCSA_HD void tok_range(bool preserve, int c, int n, int w, int* lo, int* hi) {
+  int s = c - (w - 1) / 2;
+  if (preserve) {
+    if (n <= w) {
+      *lo = 0;
+      *hi = n - 1;
+      return;
+    }
+    s = s < 0 ? 0 : (s > n - w ? n - w : s);
+    *lo = s;
+    *hi = s + w - 1;
+  } else {
+    const int e = s + w - 1;
+    *lo = s < 0 ? 0 : s;
+    *hi = e > n - 1 ? n - 1 : e;
+  }
+}
 
 // Inclusive block range [lo, hi] visible along one axis of n blocks from block c.
 LCSA_HD void win_range(int mode, int c, int n, int wb, int* lo, int* hi) {
@@ -65,11 +92,37 @@ LCSA_HD void qblock_coords(const Geom& g, int i, int* tb, int* hb, int* wb) {
   *wb = rem - (rem / g.Wb) * g.Wb;
 }
 
+// Rows (1..8) of block row hb and columns (1..8) of block column wb that lie inside the grid: blocks
+// start at the spatial origin, so only the last block row and column can be partial.
+LCSA_HD int block_rows(const Geom& g, int hb) {
+  const int r = g.H - kBlkH * hb;
+  return r < kBlkH ? r : kBlkH;
+}
+LCSA_HD int block_cols(const Geom& g, int wb) {
+  const int c = g.W - kBlkW * wb;
+  return c < kBlkW ? c : kBlkW;
+}
+
 // Visible spatial window of query block i: block rows [h0, h1], block columns [w0, w1];
-// returns the last visible temporal block.
+// returns the last visible temporal block. With a token-granular window a key block is visible when
+// some token of i sees some token of it: per axis, the union of the windows of i's tokens, which is
+// [lo(first), hi(last)] since the bounds are monotone.
 LCSA_HD int qblock_window(const Geom& g, int i, int* h0, int* h1, int* w0, int* w1) {
   int tb, hb, wb;
   qblock_coords(g, i, &tb, &hb, &wb);
+  if (token_window(g)) {
+    const bool pres = g.win_mode == kWinTokenPreserving;
+    int lo, hi, lo2, hi2;
+    tok_range(pres, 8 * hb, g.H, g.wth, &lo, &hi);
+    tok_range(pres, 8 * hb + block_rows(g, hb) - 1, g.H, g.wth, &lo2, &hi2);
+    *h0 = lo / 8;
+    *h1 = hi2 / 8;
+    tok_range(pres, 8 * wb, g.W, g.wtw, &lo, &hi);
+    tok_range(pres, 8 * wb + block_cols(g, wb) - 1, g.W, g.wtw, &lo2, &hi2);
+    *w0 = lo / 8;
+    *w1 = hi2 / 8;
+    return tb;
+  }
   win_range(g.win_mode, hb, g.Hb, g.wbh, h0, h1);
   win_range(g.win_mode, wb, g.Wb, g.wbw, w0, w1);
   return tb;
@@ -93,17 +146,6 @@ inline FastDiv make_fastdiv(uint32_t d) {
 
 LCSA_HD uint32_t fast_div(uint32_t n, const FastDiv& f) { return uint32_t((uint64_t(n) * f.m) >> f.k); }
 
-// Rows (1..8) of block row hb and columns (1..8) of block column wb that lie inside the grid: blocks
-// start at the spatial origin, so only the last block row and column can be partial.
-LCSA_HD int block_rows(const Geom& g, int hb) {
-  const int r = g.H - kBlkH * hb;
-  return r < kBlkH ? r : kBlkH;
-}
-LCSA_HD int block_cols(const Geom& g, int wb) {
-  const int c = g.W - kBlkW * wb;
-  return c < kBlkW ? c : kBlkW;
-}
-
 // A 64-token tile is one frame of a block, tile row k = 8 * y + x. A 32x32 score accumulator of
 // the 32-row tile kt of such a tile (the MFMA result layout) holds, in item v of a lane with lane
 // half hi, tile row kt*32 + 8*(v/4) + 4*hi + v%4. Items whose token lies outside the grid of a
@@ -115,6 +157,47 @@ LCSA_HD void mask_partial_tile(V& s, int kt, int hi, int rows, int cols) {
     const int y = kt * 4 + v / 4, x = 4 * hi + v % 4;
     if (!(y < rows && x < cols)) s[v] = -INFINITY;
   }
+}
+
+// Token-window mask of the same accumulator layout for a key tile whose first token sits at row h0,
+// column w0 of the grid, for a lane whose query token sees rows [lo_h, hi_h] and columns [lo_w, hi_w]
+// (also masks tokens past the grid edge, which lie outside every window).
+template <class V>
+LCSA_HD void mask_window_tile(V& s, int kt, int hi, int h0, int w0, int lo_h, int hi_h, int lo_w, int hi_w) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int hk = h0 + kt * 4 + v / 4, wk = w0 + 4 * hi + v % 4;
+    if (!(hk >= lo_h && hk <= hi_h && wk >= lo_w && wk <= hi_w)) s[v] = -INFINITY;
+  }
+}
+
+// The same token-window test with the roles swapped (the dK/dV layout: accumulator rows are query
+// tokens, the lane holds one key token at (hk, wk)): item v's query token sits at row qh0 + kt*4 + v/4,
+// column qw0 + 4*hi + v%4; it is masked when it lies outside the grid or its window misses the key.
+template <class V>
+LCSA_HD void mask_window_tile_q(V& s, int kt, int hi, int qh0, int qw0, int hk, int wk, const Geom& g) {
+  const bool pres = g.win_mode == kWinTokenPreserving;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int hq = qh0 + kt * 4 + v / 4, wq = qw0 + 4 * hi + v % 4;
+    int lh, hh, lw, hw2;
+    tok_range(pres, hq, g.H, g.wth, &lh, &hh);
+    tok_range(pres, wq, g.W, g.wtw, &lw, &hw2);
+    if (!(hq < g.H && wq < g.W && hk >= lh && hk <= hh && wk >= lw && wk <= hw2)) s[v] = -INFINITY;
+  }
+}
+
+// Whether key block (hb, wb) lies wholly inside the window of every token of query block (qhb, qwb):
+// the bounds are monotone, so the last query row / column bounds the start and the first the end.
+LCSA_HD bool block_seen_whole(const Geom& g, int qhb, int qwb, int hb, int wb) {
+  const bool pres = g.win_mode == kWinTokenPreserving;
+  int lo_last, hi_last, lo_first, hi_first;
+  tok_range(pres, kBlkH * qhb + block_rows(g, qhb) - 1, g.H, g.wth, &lo_last, &hi_last);
+  tok_range(pres, kBlkH * qhb, g.H, g.wth, &lo_first, &hi_first);
+  if (!(kBlkH * hb >= lo_last && kBlkH * hb + kBlkH - 1 <= hi_first)) return false;
+  tok_range(pres, kBlkW * qwb + block_cols(g, qwb) - 1, g.W, g.wtw, &lo_last, &hi_last);
+  tok_range(pres, kBlkW * qwb, g.W, g.wtw, &lo_first, &hi_first);
+  return kBlkW * wb >= lo_last && kBlkW * wb + kBlkW - 1 <= hi_first;
 }
 
 LCSA_HD int n_visible(const Geom& g, int i) {

@@ -49,9 +49,12 @@ lcsa_status validate_problem(const lcsa_problem* p, Geom* g) {
                 p->q_frame0 + p->q_frames, p->kv_frames);
   if (p->kv_frames % kBlkT || p->q_frames % kBlkT || p->q_frame0 % kBlkT)
     return fail(LCSA_ERR_UNSUPPORTED, "frame counts and q_frame0 must be multiples of %d", kBlkT);
-  if (p->win_mode < LCSA_WIN_NONE || p->win_mode > LCSA_WIN_PRESERVING)
+  if (p->win_mode < LCSA_WIN_NONE || p->win_mode > LCSA_WIN_TOKEN_PRESERVING)
     return fail(LCSA_ERR_INVALID, "win_mode %d is not an lcsa_win_mode", p->win_mode);
-  if (p->win_mode != LCSA_WIN_NONE) {
+  if (p->win_mode >= LCSA_WIN_TOKEN_TRUNCATED) {
+    if (p->win_h <= 0 || p->win_w <= 0)
+      return fail(LCSA_ERR_INVALID, "token window %dx%d must be positive", p->win_h, p->win_w);
+  } else if (p->win_mode != LCSA_WIN_NONE) {
     if (p->win_h <= 0 || p->win_w <= 0 || p->win_h % kBlkH || p->win_w % kBlkW ||
         (p->win_h / kBlkH) % 2 == 0 || (p->win_w / kBlkW) % 2 == 0)
       return fail(LCSA_ERR_INVALID, "window %dx%d tokens must be an odd number of 8-token blocks",
@@ -82,8 +85,11 @@ lcsa_status validate_problem(const lcsa_problem* p, Geom* g) {
     g->nkb = static_cast<int32_t>(nkb);
     g->q_tb0 = p->q_frame0 / kBlkT;
     g->win_mode = p->win_mode;
-    g->wbh = p->win_mode ? p->win_h / kBlkH : 0;
-    g->wbw = p->win_mode ? p->win_w / kBlkW : 0;
+    const bool blockwin = p->win_mode == LCSA_WIN_TRUNCATED || p->win_mode == LCSA_WIN_PRESERVING;
+    g->wbh = blockwin ? p->win_h / kBlkH : 0;
+    g->wbw = blockwin ? p->win_w / kBlkW : 0;
+    g->wth = blockwin || p->win_mode == LCSA_WIN_NONE ? 0 : p->win_h;
+    g->wtw = blockwin || p->win_mode == LCSA_WIN_NONE ? 0 : p->win_w;
   }
   return LCSA_OK;
 }

@@ -50,7 +50,19 @@ typedef enum { LCSA_BF16 = 0, LCSA_F32 = 1 } lcsa_dtype;
  * (odd), r = (w_b-1)/2. TRUNCATED keeps the blocks within r of the query block, cut at the frame
  * edge; PRESERVING slides a w_b-wide window inward at the edge (start = clamp(c-r, 0, N-w_b)), so
  * every query keeps w_b blocks per axis. The same window applies in every visible temporal block. */
-typedef enum { LCSA_WIN_NONE = 0, LCSA_WIN_TRUNCATED = 1, LCSA_WIN_PRESERVING = 2 } lcsa_win_mode;
+/* TOKEN_TRUNCATED / TOKEN_PRESERVING: the same two rules per query token instead of per block. A query
+ * token at (h, w) sees the key tokens in rows [h - (win_h-1)/2, h - (win_h-1)/2 + win_h - 1] and the
+ * like columns (win_h, win_w any positive token counts), cut at the frame edge or shifted inside. A
+ * key block is a candidate of query block i when some token of i sees some token of it; inside a kept
+ * block only the tokens in the query token's window take part. A query token that sees no token of
+ * its kept blocks gets O = 0 and lse = -inf. */
+typedef enum {
+  LCSA_WIN_NONE = 0,
+  LCSA_WIN_TRUNCATED = 1,
+  LCSA_WIN_PRESERVING = 2,
+  LCSA_WIN_TOKEN_TRUNCATED = 3,
+  LCSA_WIN_TOKEN_PRESERVING = 4
+} lcsa_win_mode;
 
 typedef struct {
   int32_t batch, heads, head_dim;  /* head_dim in {64, 128} */
@@ -60,7 +72,7 @@ typedef struct {
   int32_t q_frame0, q_frames;      /* Q holds latent frames [q_frame0, q_frame0 + q_frames) */
   int32_t blk_t, blk_h, blk_w;     /* block shape in tokens; only 2 x 8 x 8 is implemented */
   int32_t win_mode;                /* lcsa_win_mode */
-  int32_t win_h, win_w;            /* window in tokens; win/blk must be an odd integer */
+  int32_t win_h, win_w;            /* window in tokens; block modes: win/blk must be an odd integer */
   int32_t topk;                    /* > 0: K_i = min(topk, n_i); 0: K_i from keep_ratio */
   double keep_ratio;               /* (0, 1]: K_i = clamp(floor(keep_ratio * n_i + 0.5), 1, n_i) */
   float scale;                     /* softmax / block-score scale (> 0), e.g. 1/sqrt(head_dim) */

@@ -33,6 +33,11 @@ The passages leave several steps open; the readings taken here (all stated in DE
      height, width): the head dim splits into three even groups, one per axis; adjacent dims form
      the rotated pairs; frequencies theta^(-2j/dim_axis); positions are the absolute latent frame
      and the token row and column. The pages only name the embedding (sec. 2.3).
+  R11 token-granular windows (the same two rules per token): a query token at position c of an axis
+     of n tokens sees the w tokens starting at c - (w-1)//2, cut to [0, n) (truncated) or shifted
+     inside (preserving); a key block is a candidate of a query block when some token of one sees
+     some token of the other (block-causal as before); inside kept blocks only visible token pairs
+     take part; a query token that sees no kept token gets O = 0 and lse = -inf.
   R9 a grid that is not a multiple of 8 is cut into blocks from its origin; the last block row and
      column are partial. A partial block is pooled over the tokens it has, and attention over a
      kept partial block covers only those tokens. Block counts are ceil(H/8) x ceil(W/8).
@@ -55,6 +60,7 @@ import numpy as np
 BLK_T, BLK_H, BLK_W = 2, 8, 8
 BLK = BLK_T * BLK_H * BLK_W
 WIN_NONE, WIN_TRUNCATED, WIN_PRESERVING = 0, 1, 2
+WIN_TOKEN_TRUNCATED, WIN_TOKEN_PRESERVING = 3, 4
 
 
 # ----------------------------------------------------------------------------------- geometry
@@ -100,10 +106,39 @@ def window_blocks(mode, c, n, wb_size):
     raise ValueError(mode)
 
 
+def token_window(mode, c, n, w):
+    """Set of token coordinates along one axis (of n tokens) that a query token at c sees (R11)."""
+    start = c - (w - 1) // 2
+    if mode == WIN_TOKEN_TRUNCATED:
+        return {x for x in range(start, start + w) if 0 <= x < n}
+    if mode == WIN_TOKEN_PRESERVING:
+        if n <= w:
+            return set(range(n))
+        start = min(max(start, 0), n - w)
+        return set(range(start, start + w))
+    raise ValueError(mode)
+
+
+def _token_axis_blocks(p, mode, c_block, n_tok, w):
+    """Block coordinates along one axis seen by some token of block c_block (R11)."""
+    seen = set()
+    for c in range(c_block * BLK_H, min(c_block * BLK_H + BLK_H, n_tok)):
+        seen |= token_window(mode, c, n_tok, w)
+    return {x // BLK_H for x in seen}
+
+
 def visible(p):
-    """Boolean [nqb, nkb]: block-causal (R1) AND spatial window (R6), by enumeration."""
+    """Boolean [nqb, nkb]: block-causal (R1) AND spatial window (R6 / R11), by enumeration."""
     Hb, Wb = _grid(p)
     qb, kb = query_blocks(p), key_blocks(p)
+    if p.win_mode >= WIN_TOKEN_TRUNCATED:
+        vis = np.zeros((len(qb), len(kb)), dtype=bool)
+        for i, (ti, hi, wi) in enumerate(qb):
+            rows = _token_axis_blocks(p, p.win_mode, hi, p.grid_h, p.win_h)
+            cols = _token_axis_blocks(p, p.win_mode, wi, p.grid_w, p.win_w)
+            for j, (tj, hj, wj) in enumerate(kb):
+                vis[i, j] = (tj <= ti) and (hj in rows) and (wj in cols)
+        return vis
     wh = p.win_h // BLK_H if p.win_mode != WIN_NONE else 0
     ww = p.win_w // BLK_W if p.win_mode != WIN_NONE else 0
     vis = np.zeros((len(qb), len(kb)), dtype=bool)
@@ -184,9 +219,29 @@ def select(p, scores, vis=None):
 
 
 # -------------------------------------------------------------------------------- attention
+def token_pair_mask(p, qt, kt):
+    """[len(qt), len(kt)] boolean: query token qt[a] sees key token kt[b] under a token-granular
+    window (R11); all True for the block-granular modes. Token indices are raster positions in their
+    own tensors, so only the spatial coordinates matter here (causality is block-level)."""
+    if p.win_mode < WIN_TOKEN_TRUNCATED:
+        return np.ones((len(qt), len(kt)), dtype=bool)
+    hw = p.grid_h * p.grid_w
+    hq, wq = (qt % hw) // p.grid_w, qt % p.grid_w
+    hk, wk = (kt % hw) // p.grid_w, kt % p.grid_w
+    # each window is a run of consecutive coordinates: keep its first and last
+    rows = [token_window(p.win_mode, h, p.grid_h, p.win_h) for h in range(p.grid_h)]
+    cols = [token_window(p.win_mode, w, p.grid_w, p.win_w) for w in range(p.grid_w)]
+    rlo, rhi = np.array([min(r) for r in rows]), np.array([max(r) for r in rows])
+    clo, chi = np.array([min(c) for c in cols]), np.array([max(c) for c in cols])
+    mh = (hk[None, :] >= rlo[hq][:, None]) & (hk[None, :] <= rhi[hq][:, None])
+    mw = (wk[None, :] >= clo[wq][:, None]) & (wk[None, :] <= chi[wq][:, None])
+    return mh & mw
+
+
 def attend(p, q, k, v, row_ptr, col_idx, qblocks=None, bh=None):
     """Exact softmax attention of every query token of block i over all tokens of the key blocks
-    listed for row i (no token-level mask inside a selected block).
+    listed for row i (no token-level mask inside a selected block, except the token-granular window
+    of R11).
 
     q: [B, heads, Nq, d], k/v: [B, heads, Nk, d]. Returns O [B, heads, Nq, d] and lse [B, heads, Nq]
     (natural log of the softmax denominator, max-shifted); rows not requested stay NaN.
@@ -209,11 +264,14 @@ def attend(p, q, k, v, row_ptr, col_idx, qblocks=None, bh=None):
             sel = col_idx[b, h, row_ptr[i]:row_ptr[i + 1]]
             kt = np.concatenate([ktok[j] for j in sel])
             logits = p.scale * (q[b, h, qt] @ k[b, h, kt].T)      # [128, K_i*128]
+            mask = token_pair_mask(p, qt, kt)
+            logits = np.where(mask, logits, -np.inf)
             m = logits.max(axis=1, keepdims=True)
-            e = np.exp(logits - m)
+            seen = np.isfinite(m)                                  # rows that see some kept token
+            e = np.exp(logits - np.where(seen, m, 0.0))
             den = e.sum(axis=1, keepdims=True)
-            O[b, h, qt] = (e / den) @ v[b, h, kt]
-            lse[b, h, qt] = (m + np.log(den))[:, 0]
+            O[b, h, qt] = np.where(seen, (e / np.where(seen, den, 1.0)) @ v[b, h, kt], 0.0)
+            lse[b, h, qt] = np.where(seen, m + np.log(np.where(seen, den, 1.0)), -np.inf)[:, 0]
     return O, lse
 
 
@@ -245,8 +303,11 @@ def attend_bwd(p, q, k, v, row_ptr, col_idx, dO, qblocks=None, bh=None):
             sel = col_idx[b, h, row_ptr[i]:row_ptr[i + 1]]
             kt = np.concatenate([ktok[j] for j in sel])
             logits = p.scale * (q[b, h, qt] @ k[b, h, kt].T)
-            e = np.exp(logits - logits.max(axis=1, keepdims=True))
-            P = e / e.sum(axis=1, keepdims=True)                    # [128, n]
+            logits = np.where(token_pair_mask(p, qt, kt), logits, -np.inf)
+            m = logits.max(axis=1, keepdims=True)
+            seen = np.isfinite(m)                                   # rows that see some kept token
+            e = np.exp(logits - np.where(seen, m, 0.0))
+            P = e / np.where(seen, e.sum(axis=1, keepdims=True), 1.0)  # [128, n]; unseen rows are 0
             Ot = P @ v[b, h, kt]
             g = dO[b, h, qt]
             dP = g @ v[b, h, kt].T
@@ -340,6 +401,7 @@ def dense_block_causal(p, q, k, v):
     for j, blk in enumerate(key_blocks(p)):
         kblock_of[block_tokens(p, blk, 0)] = j
     mask = vis[qblock_of][:, kblock_of]                                # [Nq, Nk]
+    mask &= token_pair_mask(p, np.arange(Nq), np.arange(Nk))          # token-granular window (R11)
     logits = p.scale * np.matmul(q, np.swapaxes(k, -1, -2))
     logits = np.where(mask, logits, -np.inf)
     m = logits.max(axis=-1, keepdims=True)

@@ -14,7 +14,10 @@ Tolerances (fixed here, used by every GPU test):
               so the error measures attention only: max |O - O_ref| <= 2e-2 and
               mean |O - O_ref| <= 2e-3 at bf16 I/O; lse max abs <= 1e-3 for bf16 inputs, 1e-2 for
               fp32 inputs (the kernel rounds Q/K to bf16 on load), and sum_k exp(l - lse_gpu) = 1
-              within the same bound per row (|sum - 1| is about |lse error|).
+              within the same bound per row (|sum - 1| is about |lse error|). A row that sees fewer
+              than 128 keys (token-granular windows) gets max(that bound, 2^-8): its denominator sums
+              few bf16-rounded probabilities, each within 2^-8 of its value, with little averaging.
+              A row that sees none of its kept keys must have O = 0 and lse = -inf exactly.
 """
 from __future__ import annotations
 
@@ -109,20 +112,50 @@ def check_selection(w, gpu, ref_scores, ref_col, row_ptr):
     return near, swapped
 
 
+def visible_key_counts(w, gpu, qblocks=None, bh=None):
+    """[B, Hh, Nq]: how many tokens of its kept blocks each query token sees (token windows, partial
+    blocks); -1 where not computed."""
+    qb, kb = O.query_blocks(w), O.key_blocks(w)
+    B, Hh = gpu["col_idx"].shape[:2]
+    out = np.full((B, Hh, w.nq_tokens), -1, dtype=np.int64)
+    qblocks = range(len(qb)) if qblocks is None else qblocks
+    bh = [(b, h) for b in range(B) for h in range(Hh)] if bh is None else bh
+    ktok = [O.block_tokens(w, blk, 0) for blk in kb]
+    rp = gpu["row_ptr"]
+    for i in qblocks:
+        qt = O.block_tokens(w, qb[i], w.q_frame0)
+        for b, h in bh:
+            sel = gpu["col_idx"][b, h, rp[i]:rp[i + 1]]
+            kt = np.concatenate([ktok[j] for j in sel])
+            out[b, h, qt] = O.token_pair_mask(w, qt, kt).sum(axis=1)
+    return out
+
+
 def check_attention(w, x64, gpu, qblocks=None, bh=None):
     """Oracle attention on the GPU's kept sets for the given rows; returns error stats."""
     q, k, v = x64
     Oref, lref = O.attend(w, q, k, v, gpu["row_ptr"], gpu["col_idx"], qblocks=qblocks, bh=bh)
     rows = ~np.isnan(lref)
     Og, lg = gpu["O"], gpu["lse"]
+    # a query token that sees none of its kept tokens (token-granular windows): O = 0, lse = -inf
+    blind = rows & np.isneginf(lref)
+    assert np.all(np.isneginf(lg[blind])) and not np.any(Og[blind]), "rows without visible keys"
+    rows &= ~blind
     dO = np.abs(Og[rows] - Oref[rows])
     dl = np.abs(lg[rows] - lref[rows])
     assert np.all(np.isfinite(Og[rows])) and np.all(np.isfinite(lg[rows]))
-    stats = dict(o_max=float(dO.max()), o_mean=float(dO.mean()), lse_max=float(dl.max()), rows=int(rows.sum()))
+    stats = dict(o_max=float(dO.max()), o_mean=float(dO.mean()), lse_max=float(dl.max()), rows=int(rows.sum()),
+                 blind_rows=int(blind.sum()))
     assert stats["o_max"] <= O_MAX, stats
     assert stats["o_mean"] <= O_MEAN, stats
     lse_tol = 1e-3 if w.dtype == "bf16" else 1e-2
-    assert stats["lse_max"] <= lse_tol, stats
+    # The denominator sums the bf16-rounded probabilities (those P V uses): each is within 2^-8 of its
+    # value, so lse is within about 2^-8 of the exact one whatever the count; over many keys the
+    # roundings average out and 1e-3 holds. Rows that see fewer than 128 keys (token windows) get 2^-8.
+    few = rows & (visible_key_counts(w, gpu, qblocks, bh) < 128)
+    stats["few_key_rows"] = int(few.sum())
+    assert np.all(np.abs(lg[rows & ~few] - lref[rows & ~few]) <= lse_tol), stats
+    assert np.all(np.abs(lg[few] - lref[few]) <= max(lse_tol, 2.0 ** -8)), stats
     # softmax normalisation with the GPU's lse, for a few rows
     qb, kb = O.query_blocks(w), O.key_blocks(w)
     qblocks = list(range(len(qb))) if qblocks is None else list(qblocks)
@@ -130,9 +163,11 @@ def check_attention(w, x64, gpu, qblocks=None, bh=None):
     for i in qblocks[:4]:
         qt = O.block_tokens(w, qb[i], w.q_frame0)
         kt = np.concatenate([O.block_tokens(w, kb[j], 0) for j in gpu["col_idx"][b, h, gpu["row_ptr"][i]:gpu["row_ptr"][i + 1]]])
-        l = w.scale * q[b, h, qt] @ k[b, h, kt].T
-        sums = np.exp(l - lg[b, h, qt][:, None]).sum(axis=1)
-        assert np.all(np.abs(sums - 1.0) <= lse_tol), sums
+        l = np.where(O.token_pair_mask(w, qt, kt), w.scale * q[b, h, qt] @ k[b, h, kt].T, -np.inf)
+        seen = np.isfinite(lg[b, h, qt])
+        sums = np.exp(l[seen] - lg[b, h, qt][seen][:, None]).sum(axis=1)
+        tol = np.where(np.isfinite(l[seen]).sum(axis=1) < 128, max(lse_tol, 2.0 ** -8), lse_tol)
+        assert np.all(np.abs(sums - 1.0) <= tol), sums
     return stats
 
 

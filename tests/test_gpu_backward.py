@@ -33,9 +33,11 @@ pytestmark = pytest.mark.gpu
 REL_MAX, REL_MEAN = 1e-2, 1e-2
 
 
-def run(w, seed):
+def run(w, seed, negate_k=False):
     p = lcsa.problem(w)
     x = inputs.make_inputs(w, seed)
+    if negate_k:
+        x["k"] = x["k"] ^ np.uint16(0x8000)   # bf16 sign bit
     g = inputs.make_grad(w, seed)
     q, k, v, d_o = (to_device(a) for a in (x["q"], x["k"], x["v"], g))
     out = lcsa.forward(p, q, k, v)
@@ -108,6 +110,12 @@ SMALL = [
     W.Workload("bwd_ragged_13x10_d64_pres", 1, 2, 64, 13, 10, 4, 0, 4, win_mode=2, win_h=24, win_w=24,
                keep_ratio=0.5),
     W.Workload("bwd_ragged_3x5", 1, 1, 128, 3, 5, 6, 4, 2, topk=2),
+    # token-granular windows (the last: one kept block per row under a 3x3 window)
+    W.Workload("bwd_tokwin_trunc_24x40_w13x17", 1, 2, 128, 24, 40, 4, 2, 2, win_mode=3, win_h=13, win_w=17,
+               keep_ratio=0.5),
+    W.Workload("bwd_tokwin_pres_21x37_w20x9", 1, 2, 128, 21, 37, 6, 4, 2, win_mode=4, win_h=20, win_w=9,
+               keep_ratio=0.4),
+    W.Workload("bwd_tokwin_w3_topk1", 1, 2, 64, 24, 32, 4, 2, 2, win_mode=3, win_h=3, win_w=3, topk=1),
 ]
 
 
@@ -124,6 +132,22 @@ def test_backward_small(w):
     if w.topk == 1:
         assert stats["unkept_key_blocks"] > 0
     report(w.name, stats)
+
+
+def test_backward_rows_without_keys():
+    """Token window 3x3, one kept block per row, K negated so the kept block is a neighbour: most
+    query tokens see no kept key (forward O = 0, lse = -inf) and must get exactly zero dQ; the
+    others, and dK / dV, meet the usual bar."""
+    w = W.Workload("bwd_tokwin_blind_24x32_w3_topk1", 1, 2, 128, 24, 32, 4, 2, 2, win_mode=3, win_h=3, win_w=3,
+                   topk=1)
+    r = run(w, 0, negate_k=True)
+    q, k, v = r["x64"]
+    dQ, dK, dV = O.attend_bwd(w, q, k, v, r["row_ptr"], r["col"], r["g64"])
+    blind = np.all(dQ == 0.0, axis=-1)
+    assert blind.sum() > 0 and not np.any(r["dq"][blind])
+    mk = np.ones(dK.shape[:3], dtype=bool)
+    report(w.name, {"blind_rows": int(blind.sum()), "dq": compare("dq", r["dq"], dQ, ~blind),
+                    "dk": compare("dk", r["dk"], dK, mk), "dv": compare("dv", r["dv"], dV, mk)})
 
 
 def test_backward_full_selection_matches_dense():

@@ -14,7 +14,7 @@ from block_sparse_causal_lcsa_amd import inputs, lcsa
 from block_sparse_causal_lcsa_amd import workloads as W
 from oracle import lcsa_oracle as O
 
-from parity import check_attention, full_check, run_gpu, to_device, from_device
+from parity import check_attention, check_selection, full_check, run_gpu, to_device, from_device
 
 pytestmark = pytest.mark.gpu
 
@@ -127,6 +127,51 @@ RAGGED = [
 @pytest.mark.parametrize("w", RAGGED, ids=lambda w: w.name)
 def test_ragged_grids(w):
     report(w.name, full_check(w, 0))
+
+
+# Token-granular windows (per-token masks inside kept blocks, R11), both rules, even and odd sizes,
+# with a ragged grid, d = 64 and fp32 I/O
+TOKEN_WINDOWS = [
+    W.Workload("tokwin_trunc_24x40_w13x17", 1, 2, 128, 24, 40, 4, 2, 2, win_mode=3, win_h=13, win_w=17,
+               keep_ratio=0.5),
+    W.Workload("tokwin_pres_21x37_w20x9", 1, 2, 128, 21, 37, 6, 4, 2, win_mode=4, win_h=20, win_w=9,
+               keep_ratio=0.4),
+    W.Workload("tokwin_trunc_16x24_w6_d64_b2", 2, 2, 64, 16, 24, 4, 0, 4, win_mode=3, win_h=6, win_w=6, topk=2),
+    W.Workload("tokwin_pres_16x24_f32", 1, 2, 128, 16, 24, 4, 2, 2, dtype="f32", win_mode=4, win_h=11, win_w=24,
+               keep_ratio=0.5),
+]
+
+
+@pytest.mark.parametrize("w", TOKEN_WINDOWS, ids=lambda w: w.name)
+def test_token_windows(w):
+    report(w.name, full_check(w, 0))
+
+
+def test_token_window_rows_without_keys():
+    """One kept block per row under a 3x3-token window: query tokens deep inside their block see none
+    of a neighbouring kept block, and must get O = 0 and lse = -inf."""
+    w = W.Workload("tokwin_blind_24x32_w3_topk1", 1, 2, 128, 24, 32, 4, 2, 2, win_mode=3, win_h=3, win_w=3,
+                   topk=1)
+    x = inputs.make_inputs(w, 0)
+    x["k"] = x["k"] ^ np.uint16(0x8000)   # K negated (bf16 sign bit): a query block's own block scores lowest
+    gpu = run_gpu(w, x)
+    x64 = [inputs.to_f64(x[n]) for n in "qkv"]
+    vis = O.visible(w)
+    s = O.block_scores(w, O.pool(w, x64[0], "q"), O.pool(w, x64[1], "k"), vis)
+    rp, col = O.select(w, s, vis)
+    near, swapped = check_selection(w, gpu, s, col, rp)
+    stats = check_attention(w, x64, gpu)
+    assert stats["blind_rows"] > 0
+    stats.update(near_tie_rows=near, swapped_rows=swapped)
+    report(w.name, stats)
+
+
+def test_uhd_token_window_72():
+    """The 1536x2688 chunk with a 72x72-token window per query token (truncated), sampled rows."""
+    w = W.UHD_TRUNC.replace(name="chunk_1536x2688_tokwin72_truncated", win_mode=3, win_h=72, win_w=72)
+    Wb = w.grid_w // 8
+    qb = sorted({0, Wb - 1, 5 * Wb + 10, 11 * Wb + 20, w.nqb - 1} | set(sample_blocks(w, 4)))
+    report(w.name, full_check(w, 0, qblocks=qb, bh=[(0, h) for h in (0, 7)], scores=False))
 
 
 def test_hd_720x1280_ragged():

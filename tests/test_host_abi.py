@@ -60,12 +60,14 @@ def random_problems(n, seed):
         kvf = 2 * int(rng.integers(1, 5))
         qf = 2 * int(rng.integers(1, kvf // 2 + 1))
         q0 = 2 * int(rng.integers(0, (kvf - qf) // 2 + 1))
-        mode = int(rng.integers(0, 3))
+        mode = int(rng.integers(0, 5))   # none, block truncated / preserving, token truncated / preserving
         wb_h, wb_w = 2 * int(rng.integers(0, 5)) + 1, 2 * int(rng.integers(0, 5)) + 1
+        if mode >= 3:                      # token windows: any positive size, in blocks' stead
+            wb_h, wb_w = int(rng.integers(1, 40)) / 8, int(rng.integers(1, 40)) / 8
         topk = int(rng.integers(0, 6))
         rho = float(rng.choice([0.05, 0.136, 0.25, 1 / 3, 0.5, 0.77, 1.0]))
         out.append(W.Workload("r", 1, 2, 64, 8 * Hb - dh, 8 * Wb - dw, kvf, q0, qf, win_mode=mode,
-                              win_h=8 * wb_h if mode else 0, win_w=8 * wb_w if mode else 0,
+                              win_h=int(8 * wb_h) if mode else 0, win_w=int(8 * wb_w) if mode else 0,
                               topk=topk, keep_ratio=rho))
     return out
 
@@ -98,6 +100,7 @@ BASE = W.CHUNK_768
     (dict(win_mode=1, win_h=64, win_w=72), lcsa.LCSA_ERR_INVALID),
     (dict(win_mode=2, win_h=0, win_w=72), lcsa.LCSA_ERR_INVALID),
     (dict(win_mode=5, win_h=72, win_w=72), lcsa.LCSA_ERR_INVALID),
+    (dict(win_mode=3, win_h=0, win_w=72), lcsa.LCSA_ERR_INVALID),
 ])
 def test_invalid_problems_rejected_on_host(change, status):
     _check_rejected(BASE.replace(**change), status)

@@ -107,12 +107,14 @@ struct TileB {
   static constexpr int ELEMS = kTok * D;
 };
 
+// Loads one tile with four waves; `wave` (0..3, wave-uniform) is this wave's share.
 template <int D>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* tile, uint32_t tst, uint32_t base_tok,
-                                          int W) {
+                                          int W, int wave) {
   constexpr int CPR = TileB<D>::CPR;
   // the scalar offset must be wave-uniform in registers the compiler can see as such
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  wave = __builtin_amdgcn_readfirstlane(wave);
   base_tok = __builtin_amdgcn_readfirstlane(base_tok);
 #pragma unroll
   for (int it = 0; it < TileB<D>::LOADS; ++it) {
@@ -170,26 +172,6 @@ __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Position of op j in the MFMA list of one 64-row sub-tile (two 32-row tiles t): group A (NA ops per
-// tile) and group B (NB ops per tile), ordered A(0) | LEAD ops of A(1) | the other A(1) ops evenly
-// interleaved with B(0) | B(1). The vector step of tile 0 goes before the interleaved part, that of
-// tile 1 before B(1).
-struct OpPos {
-  int grp, t, o;
-};
-template <int NA, int NB, int LEAD>
-constexpr OpPos op_pos(int j) {
-  constexpr int MIX0 = NA + LEAD, MIXN = NA - LEAD + NB;
-  if (j < NA) return {0, 0, j};
-  if (j < MIX0) return {0, 1, j - NA};
-  if (j < MIX0 + MIXN) {
-    const int k = j - MIX0, nb = (k * NB) / MIXN;  // B ops placed before position k
-    if (((k + 1) * NB) / MIXN > nb) return {1, 0, nb};
-    return {0, 1, LEAD + (k - nb)};
-  }
-  return {1, 1, j - MIX0 - MIXN};
 }
 
 // Wave-uniform 32-bit loads through the scalar cache (selection lists, row pointers).
@@ -421,8 +403,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int lim_c = 136, lim_n = 136;
   if (total > 0) {
     const uint32_t b0 = base_of(0, ok_n, lim_n);
-    load_tile<D>(krs, kbuf, kst, b0, g.W);
-    load_tile<D>(vrs, vbuf, vst, b0, g.W);
+    load_tile<D>(krs, kbuf, kst, b0, g.W, wave);
+    load_tile<D>(vrs, vbuf, vst, b0, g.W, wave);
   }
   for (int m = 0; m < total; ++m) {
     ok_c = ok_n;
@@ -431,8 +413,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     tile_barrier();
     if (m + 1 < total) {
       const uint32_t bn = base_of(m + 1, ok_n, lim_n);
-      load_tile<D>(krs, kbuf + ((m + 1) & 1) * TE, kst, bn, g.W);
-      load_tile<D>(vrs, vbuf + ((m + 1) & 1) * TE, vst, bn, g.W);
+      load_tile<D>(krs, kbuf + ((m + 1) & 1) * TE, kst, bn, g.W, wave);
+      load_tile<D>(vrs, vbuf + ((m + 1) & 1) * TE, vst, bn, g.W, wave);
     }
     step(kbuf + (m & 1) * TE, vbuf + (m & 1) * TE, ok_c, lim_c);
   }
@@ -452,153 +434,127 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ----------------------------------------------------------------------------------------- dkdv
+// dK/dV with two waves per key tile on one SIMD (8 waves, 512 lanes, 128 keys per workgroup): role 0
+// (waves 0-3) computes S = Q K^T, P = 2^(c S - lse2) and dV^T += dO^T P; role 1 (waves 4-7) computes
+// dP = dO V^T, dS = P (dP - Delta) and dK^T += Q^T dS, with P passed from its partner through LDS.
+// Each wave holds one accumulator set (dV or dK) and one operand set (K or V), so two waves fit a
+// SIMD and one wave's vector work overlaps the other's matrix work. Two barriers per sub-tile:
+// the first publishes the sub-tile's Q/dO tiles, the second the probabilities.
 template <int D, int MASK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_split_kernel(BwdArgs a) {
   constexpr int DS = D / 16, DT = D / 32;
   constexpr int TE = TileB<D>::ELEMS;
-  constexpr int NBUF = 3;                          // stages: the loads of m + 1 and m + 2 run during m
-  constexpr int PER = 2 * TileB<D>::LOADS + 2;     // vector-memory ops per wave per stage
-  __shared__ __attribute__((aligned(16))) uint16_t qbuf[NBUF * TE];
-  __shared__ __attribute__((aligned(16))) uint16_t gbuf[NBUF * TE];
-  __shared__ __attribute__((aligned(16))) float rlbuf[NBUF * 2 * kTok];  // per stage: [lse2 | delta] of its 64 queries
+  constexpr int kLook = 4;
+  __shared__ __attribute__((aligned(16))) uint16_t qbuf[2 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t gbuf[2 * TE];
+  __shared__ __attribute__((aligned(16))) float rlbuf[2 * 2 * kTok];   // per stage: [lse2 | delta]
+  __shared__ __attribute__((aligned(16))) float pbuf[4 * 2 * 16 * 64];  // per key tile: P, [t][v][lane]
   const Geom& g = a.g;
   const int bh = xcd_order() / g.nkb, j = xcd_order() - bh * g.nkb;
   const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int role = wave >> 2, kr = wave & 3;       // role 0: S, P, dV; role 1: dP, dS, dK; key tile kr
   const int ktr = j / g.bpt, krem = j - (j / g.bpt) * g.bpt;
   const int khb = krem / g.Wb, kwb = krem - (krem / g.Wb) * g.Wb;
-  int krow = 32 * wave + l32;
-  const bool k_in = MASK != kMaskNone ? row_inside(g, khb, kwb, 32 * wave + l32, &krow) : true;
+  int krow = 32 * kr + l32;
+  const bool k_in = MASK != kMaskNone ? row_inside(g, khb, kwb, 32 * kr + l32, &krow) : true;
   const int ktok = block_token(g, ktr, khb, kwb, krow);
   const int hk = kBlkH * khb + ((krow >> 3) & 7), wk = kBlkW * kwb + (krow & 7);  // this lane's key token
 
-  bf16x8 kf[DS], vf[DS];  // B operands: this lane's key row
+  bf16x8 opf[DS];  // B operands: this lane's key row of K (role 0) or V (role 1)
   {
-    const uint16_t* ks = a.k + b * a.ksb + h * a.ksh + int64_t(ktok) * a.kst + 8 * hi;
-    const uint16_t* vs = a.v + b * a.vsb + h * a.vsh + int64_t(ktok) * a.vst + 8 * hi;
+    const uint16_t* src = role == 0 ? a.k + b * a.ksb + h * a.ksh + int64_t(ktok) * a.kst
+                                    : a.v + b * a.vsb + h * a.vsh + int64_t(ktok) * a.vst;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      kf[s] = *reinterpret_cast<const bf16x8*>(ks + 16 * s);
-      vf[s] = *reinterpret_cast<const bf16x8*>(vs + 16 * s);
-    }
+    for (int s = 0; s < DS; ++s) opf[s] = *reinterpret_cast<const bf16x8*>(src + 8 * hi + 16 * s);
   }
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + b * a.qsb + h * a.qsh, a.q_span);
-  const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.dout + b * a.dsb + h * a.dsh, a.do_span);
-  const uint32_t qst = uint32_t(a.qst), dst = uint32_t(a.dst);
+  // role 0 loads the Q tiles and lse2, role 1 the dO tiles and Delta
+  const __amdgpu_buffer_rsrc_t trs = role == 0 ? make_rsrc(a.q + b * a.qsb + h * a.qsh, a.q_span)
+                                               : make_rsrc(a.dout + b * a.dsb + h * a.dsh, a.do_span);
+  const uint32_t tst = role == 0 ? uint32_t(a.qst) : uint32_t(a.dst);
+  const float* rsrc = role == 0 ? a.lse2 : a.delta;
+  const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rsrc + int64_t(bh) * a.nq_tok, uint32_t(a.nq_tok) * 4u);
+  uint16_t* tbuf = role == 0 ? qbuf : gbuf;
   const uint32_t hw = uint32_t(g.H) * uint32_t(g.W);
   const const_i32* cp = (const const_i32*)(a.col_ptr) + int64_t(bh) * (g.nkb + 1);
   const int beg = cp[j], nrow = cp[j + 1] - beg;
   const const_i32* rows = (const const_i32*)(a.row_of) + int64_t(bh) * a.nnz + beg;
-  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.lse2 + int64_t(bh) * a.nq_tok, uint32_t(a.nq_tok) * 4u);
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.delta + int64_t(bh) * a.nq_tok, uint32_t(a.nq_tok) * 4u);
+  float* pmine = pbuf + kr * (2 * 16 * 64);
 
-  f32x16 dk[DT], dv[DT];
+  f32x16 acc[DT];  // dV^T (role 0) or dK^T (role 1)
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dk[dt] = f32x16{};
-    dv[dt] = f32x16{};
-  }
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-  // sub-tile m = frame m%2 of query block rows[m/2]; Q is stored from the query block's own frames
   auto qbase_of = [&](int m) -> uint32_t {
     const int i = rows[m >> 1];
     const int tr = i / g.bpt, rem = i - (i / g.bpt) * g.bpt;
     const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
     return uint32_t((kBlkT * tr * g.H + kBlkH * hb) * g.W + kBlkW * wb) + uint32_t(m & 1) * hw;
   };
-  // stage m: Q and dO tiles of sub-tile m, and lse2 / delta of its 64 queries (each wave 16 of them)
   auto issue = [&](int m) {
-    const int sb = m % NBUF;
+    const int sb = m & 1;
     const uint32_t bn = __builtin_amdgcn_readfirstlane(qbase_of(m));
-    load_tile<D>(qrs, qbuf + sb * TE, qst, bn, g.W);
-    load_tile<D>(grs, gbuf + sb * TE, dst, bn, g.W);
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    float* rl = rlbuf + sb * 2 * kTok + 16 * wv;
+    load_tile<D>(trs, tbuf + sb * TE, tst, bn, g.W, kr);
+    float* rl = rlbuf + sb * 2 * kTok + role * kTok + 16 * kr;
     if (lane < 16) {
-      const int r = 16 * wv + lane;
+      const int r = 16 * kr + lane;
       const uint32_t voff = uint32_t((r >> 3) * g.W + (r & 7)) * 4u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (__attribute__((address_space(3))) void*)(rl), 4, voff,
-                                               bn * 4u, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)(rl + kTok), 4, voff,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rrs, (__attribute__((address_space(3))) void*)(rl), 4, voff,
                                                bn * 4u, 0, 0);
     }
   };
-  // One 64-query sub-tile = two 32-query tiles t. Per tile: NA products S = Q K^T and dP = dO V^T
-  // (group A), the vector step P = 2^(c S - lse2), dS = P (dP - Delta), and NB products
-  // dV^T += dO^T P, dK^T += Q^T dS (group B), issued as one MFMA list (op_pos) whose LDS operands
-  // are read kLook MFMAs ahead.
-  auto step = [&](const uint16_t* Qt, const uint16_t* Gt, const float* rl, int lim) __attribute__((always_inline)) {
-    // LEAD = 0: the vector step of tile 0 follows A(0) directly (other orders and read-ahead depths
-    // from 4 to 8 measured within 3%)
-    constexpr int NA = 2 * DS, NB = 4 * DT, LEAD = 0, MIX0 = NA + LEAD, MIXN = NA - LEAD + NB;
-    constexpr int NOPS = 2 * NA + 2 * NB;
-    constexpr int kLook = 4;
-    f32x16 sc[2], dp[2];
-    bf16x8 pb[2][2], db[2][2];
-    // A op o: (o & 1) ? dP (dO, V) : S (Q, K), d step o / 2.
-    // B op o: (o & 1) ? dK (Q^T, dS) : dV (dO^T, P); d tile (o / 2) % DT, half (o / 2) / DT.
-    auto load = [&](auto jc) __attribute__((always_inline)) -> bf16x8 {
-      constexpr OpPos q = op_pos<NA, NB, LEAD>(decltype(jc)::value);
-      if constexpr (q.grp == 0) return row_frag<D>((q.o & 1) ? Gt : Qt, q.t, q.o >> 1);
-      else return tr_frag<D>((q.o & 1) ? Qt : Gt, q.t, (q.o >> 1) / DT, (q.o >> 1) % DT);
-    };
-    // item v of tile t is query row t*32 + (v/4)*8 + 4*hi + v%4 of the sub-tile
-    auto vec = [&](int t) __attribute__((always_inline)) {
-      if constexpr (MASK == kMaskRagged) {
-        if (lim != 16 * kBlkH + kBlkW) mask_partial_tile(sc[t], t, hi, lim >> 4, lim & 15);  // queries outside the grid
-      }
-      if constexpr (MASK == kMaskWindow) {
-        if (lim >= 0)  // query tokens whose window misses this lane's key, or outside the grid
-          mask_window_tile_q(sc[t], t, hi, kBlkH * (lim >> 16), kBlkW * (lim & 0xffff), hk, wk, g);
-      }
-      f32x16 pv, ds;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int r0 = t * 32 + g4 * 8 + 4 * hi;
-        const float4 l4 = *reinterpret_cast<const float4*>(rl + r0);
-        const float4 d4 = *reinterpret_cast<const float4*>(rl + kTok + r0);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * g4 + e;
-          // a query row that sees no key (lse = -inf) gets P = 0
-          const float nl = MASK == kMaskWindow && lv[e] == -INFINITY ? -INFINITY : -lv[e];
-          pv[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.c, nl));
-          ds[v] = pv[v] * (dp[t][v] - dv4[e]);
-        }
-      }
-      pack_b(pv, pb[t]);
-      pack_b(ds, db[t]);
-    };
-    sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
+  // item v of tile t of a score accumulator is query row t*32 + (v/4)*8 + 4*hi + v%4 of the sub-tile
+  auto mask_rows = [&](f32x16& x, int t, int lim) __attribute__((always_inline)) {
+    if constexpr (MASK == kMaskRagged) {
+      if (lim != 16 * kBlkH + kBlkW) mask_partial_tile(x, t, hi, lim >> 4, lim & 15);
+    }
+    if constexpr (MASK == kMaskWindow) {
+      if (lim >= 0) mask_window_tile_q(x, t, hi, kBlkH * (lim >> 16), kBlkW * (lim & 0xffff), hk, wk, g);
+    }
+  };
+  // NA = 2 * DS products of the first phase (tile t = o / DS, d step o % DS) and NB = 4 * DT of the
+  // second (tile t = o / (2 DT), half h2 = (o / DT) & 1, d tile o % DT), operands read kLook ahead
+  constexpr int NA = 2 * DS, NB = 4 * DT;
+  auto phase1 = [&](const uint16_t* T, f32x16 (&x)[2]) __attribute__((always_inline)) {
+    x[0] = x[1] = f32x16{};
     bf16x8 fr[kLook];
-    static_for<kLook>([&](auto jc) __attribute__((always_inline)) { fr[decltype(jc)::value] = load(jc); });
-    static_for<NOPS>([&](auto jc) __attribute__((always_inline)) {
-      constexpr int j = decltype(jc)::value;
-      constexpr OpPos q = op_pos<NA, NB, LEAD>(j);
-      if constexpr (j == MIX0) vec(0);
-      if constexpr (j == MIX0 + MIXN) vec(1);
-      const bf16x8 f = fr[j % kLook];
-      if constexpr (j + kLook < NOPS) fr[j % kLook] = load(std::integral_constant<int, j + kLook>{});
-      if constexpr (q.grp == 0) {
-        if constexpr (q.o & 1) dp[q.t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, vf[q.o >> 1], dp[q.t], 0, 0, 0);
-        else sc[q.t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, kf[q.o >> 1], sc[q.t], 0, 0, 0);
-      } else {
-        constexpr int dt = (q.o >> 1) % DT, h2 = (q.o >> 1) / DT;
-        if constexpr (q.o & 1) dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, db[q.t][h2], dk[dt], 0, 0, 0);
-        else dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pb[q.t][h2], dv[dt], 0, 0, 0);
-      }
+    static_for<kLook>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int o = decltype(jc)::value;
+      fr[o] = row_frag<D>(T, o / DS, o % DS);
+    });
+    static_for<NA>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int o = decltype(jc)::value;
+      const bf16x8 f = fr[o % kLook];
+      if constexpr (o + kLook < NA) fr[o % kLook] = row_frag<D>(T, (o + kLook) / DS, (o + kLook) % DS);
+      x[o / DS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, opf[o % DS], x[o / DS], 0, 0, 0);
+    });
+  };
+  auto phase2 = [&](const uint16_t* T, const bf16x8 (&bop)[2][2]) __attribute__((always_inline)) {
+    bf16x8 fr[kLook];
+    static_for<kLook>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int o = decltype(jc)::value;
+      fr[o] = tr_frag<D>(T, o / (2 * DT), (o / DT) & 1, o % DT);
+    });
+    static_for<NB>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int o = decltype(jc)::value;
+      const bf16x8 f = fr[o % kLook];
+      if constexpr (o + kLook < NB)
+        fr[o % kLook] = tr_frag<D>(T, (o + kLook) / (2 * DT), ((o + kLook) / DT) & 1, (o + kLook) % DT);
+      acc[o % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, bop[o / (2 * DT)][(o / DT) & 1], acc[o % DT], 0, 0, 0);
     });
   };
 
-  // sub-tile m lives in stage buffer m % NBUF, loaded NBUF - 1 sub-tiles ahead
   const int total = 2 * nrow;
-  for (int m = 0; m < NBUF - 1 && m < total; ++m) issue(m);
+  if (total > 0) issue(0);
   for (int m = 0; m < total; ++m) {
-    wait_stages<PER>(min(total - 1 - m, NBUF - 2));  // stage m has landed for this wave
-    tile_barrier();                                  // ... and for every wave; stage m - 1 is free
-    if (m + NBUF - 1 < total) issue(m + NBUF - 1);
-    const int sb = m % NBUF;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stage m has landed for this wave
+    tile_barrier();                                    // ... for every wave; stage m - 1 and P are free
+    if (m + 1 < total) issue(m + 1);
+    const int sb = m & 1;
+    const uint16_t* Qt = qbuf + sb * TE;
+    const uint16_t* Gt = gbuf + sb * TE;
+    const float* rl = rlbuf + sb * 2 * kTok;
     int lim = 136;
     if constexpr (MASK == kMaskRagged) lim = block_lim(g, rows[m >> 1]);
     if constexpr (MASK == kMaskWindow) {
@@ -606,22 +562,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       lim = block_seen_whole(g, qhb, qwb, khb, kwb) && block_rows(g, qhb) == kBlkH && block_cols(g, qwb) == kBlkW
                 ? -1 : ((qhb << 16) | qwb);
     }
-    step(qbuf + sb * TE, gbuf + sb * TE, rlbuf + sb * 2 * kTok, lim);
+    f32x16 x[2];
+    bf16x8 bop[2][2];
+    if (role == 0) {
+      phase1(Qt, x);  // S = Q K^T
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        mask_rows(x[t], t, lim);
+        f32x16 pv;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(rl + t * 32 + g4 * 8 + 4 * hi);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // a query row that sees no key (lse = -inf) gets P = 0
+            const float nl = MASK == kMaskWindow && lv[e] == -INFINITY ? -INFINITY : -lv[e];
+            pv[4 * g4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[t][4 * g4 + e], a.c, nl));
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pmine[(t * 16 + v) * 64 + lane] = pv[v];
+        pack_b(pv, bop[t]);
+      }
+      tile_barrier();    // P published
+      phase2(Gt, bop);   // dV^T += dO^T P
+    } else {
+      phase1(Gt, x);     // dP = dO V^T
+      tile_barrier();    // P published
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x16 ds;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 d4 = *reinterpret_cast<const float4*>(rl + kTok + t * 32 + g4 * 8 + 4 * hi);
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * g4 + e;
+            ds[v] = pmine[(t * 16 + v) * 64 + lane] * (x[t][v] - dv4[e]);
+          }
+        }
+        pack_b(ds, bop[t]);
+      }
+      phase2(Qt, bop);   // dK^T += Q^T dS
+    }
   }
 
   if (!k_in) return;  // a key row outside the grid (partial block) has no gradient
-  float* ok_ = a.dk + (int64_t(bh) * a.nk_tok + ktok) * D;
-  float* ov_ = a.dv + (int64_t(bh) * a.nk_tok + ktok) * D;
+  float* out = (role == 0 ? a.dv : a.dk) + (int64_t(bh) * a.nk_tok + ktok) * D;
+  const float sc = role == 0 ? 1.f : a.scale;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d0 = dt * 32 + 8 * g4 + 4 * hi;
-      *reinterpret_cast<float4*>(ok_ + d0) =
-          make_float4(dk[dt][4 * g4] * a.scale, dk[dt][4 * g4 + 1] * a.scale, dk[dt][4 * g4 + 2] * a.scale,
-                      dk[dt][4 * g4 + 3] * a.scale);
-      *reinterpret_cast<float4*>(ov_ + d0) =
-          make_float4(dv[dt][4 * g4], dv[dt][4 * g4 + 1], dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3]);
+      *reinterpret_cast<float4*>(out + d0) =
+          make_float4(acc[dt][4 * g4] * sc, acc[dt][4 * g4 + 1] * sc, acc[dt][4 * g4 + 2] * sc, acc[dt][4 * g4 + 3] * sc);
     }
 }
 
@@ -738,27 +735,28 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
   csc_kernel<<<bhn, 1024, 0, s>>>(a);
   const bool ragged = (g.H % kBlkH) != 0 || (g.W % kBlkW) != 0;
   const int mask = token_window(g) ? kMaskWindow : (ragged ? kMaskRagged : kMaskNone);
+#define DKDV_LAUNCH(DD, MM) dkdv_split_kernel<DD, MM><<<bhn * g.nkb, 512, 0, s>>>(a)
   if (p->head_dim == 128) {
     if (mask == kMaskWindow) {
       dq_kernel<128, kMaskWindow><<<bhn * g.nqb, 256, 0, s>>>(a);
-      dkdv_kernel<128, kMaskWindow><<<bhn * g.nkb, 256, 0, s>>>(a);
+      DKDV_LAUNCH(128, kMaskWindow);
     } else if (mask == kMaskRagged) {
       dq_kernel<128, kMaskRagged><<<bhn * g.nqb, 256, 0, s>>>(a);
-      dkdv_kernel<128, kMaskRagged><<<bhn * g.nkb, 256, 0, s>>>(a);
+      DKDV_LAUNCH(128, kMaskRagged);
     } else {
       dq_kernel<128, kMaskNone><<<bhn * g.nqb, 256, 0, s>>>(a);
-      dkdv_kernel<128, kMaskNone><<<bhn * g.nkb, 256, 0, s>>>(a);
+      DKDV_LAUNCH(128, kMaskNone);
     }
   } else {
     if (mask == kMaskWindow) {
       dq_kernel<64, kMaskWindow><<<bhn * g.nqb, 256, 0, s>>>(a);
-      dkdv_kernel<64, kMaskWindow><<<bhn * g.nkb, 256, 0, s>>>(a);
+      DKDV_LAUNCH(64, kMaskWindow);
     } else if (mask == kMaskRagged) {
       dq_kernel<64, kMaskRagged><<<bhn * g.nqb, 256, 0, s>>>(a);
-      dkdv_kernel<64, kMaskRagged><<<bhn * g.nkb, 256, 0, s>>>(a);
+      DKDV_LAUNCH(64, kMaskRagged);
     } else {
       dq_kernel<64, kMaskNone><<<bhn * g.nqb, 256, 0, s>>>(a);
-      dkdv_kernel<64, kMaskNone><<<bhn * g.nkb, 256, 0, s>>>(a);
+      DKDV_LAUNCH(64, kMaskNone);
     }
   }
   return hip_status(hipGetLastError(), "lcsa_attn_bwd launch");

@@ -117,7 +117,7 @@ def visible_key_counts(w, gpu, qblocks=None, bh=None):
     blocks); -1 where not computed."""
     qb, kb = O.query_blocks(w), O.key_blocks(w)
     B, Hh = gpu["col_idx"].shape[:2]
-    out = np.full((B, Hh, w.nq_tokens), -1, dtype=np.int64)
+    out = np.full((B, Hh, w.q_frames * w.grid_h * w.grid_w), -1, dtype=np.int64)
     qblocks = range(len(qb)) if qblocks is None else qblocks
     bh = [(b, h) for b in range(B) for h in range(Hh)] if bh is None else bh
     ktok = [O.block_tokens(w, blk, 0) for blk in kb]

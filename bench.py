@@ -25,12 +25,17 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SRC = os.path.join(ROOT, "block_sparse_causal_lcsa_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "block_sparse_causal_lcsa_amd", "csrc")
+# the sources of the attention kernel whose HBM traffic the committed counter summary records
+KERNEL_SRCS = ["attn_fwd_impl.h", "attn_fwd_dense.hip", "attn_fwd.hip"]
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(workload: str):

@@ -16,12 +16,17 @@ OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblcsa.so")
 ARCH = "gfx950"
 
-KERNELS = ["pool.hip", "score_select.hip", "attn_fwd.hip", "attn_bwd.hip", "stream.hip", "rope.hip"]
+KERNELS = ["pool.hip", "score_select.hip", "attn_fwd.hip", "attn_fwd_dense.hip", "attn_bwd.hip", "stream.hip",
+           "rope.hip"]
 HOST = ["lcsa_host.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 # Packed fp32 VALU ops are kept out of every device build.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
+# Per-unit extra flags. The unmasked attention kernel runs 7% faster under the iterative ILP machine
+# scheduler (LDS operand reads spread between the MFMAs); the other units are no faster with it, and
+# the masked attention variants spill more registers.
+EXTRA = {"attn_fwd_dense.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _run(cmd):
@@ -37,7 +42,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in KERNELS:
         obj = os.path.join(OUT, src.replace(".hip", ".o"))
-        jobs.append(["hipcc", *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append(["hipcc", *COMMON, *DEVICE, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST:
         obj = os.path.join(OUT, src.replace(".cpp", ".o"))
         # host only; fp64 keep-ratio rule evaluated without contraction

@@ -44,9 +44,9 @@ lcsa_status validate_problem(const lcsa_problem* p, Geom* g) {
   if (p->grid_h < 1 || p->grid_w < 1) return fail(LCSA_ERR_INVALID, "grid must be positive");
   if (p->kv_frames < 1 || p->q_frames < 1 || p->q_frame0 < 0)
     return fail(LCSA_ERR_INVALID, "frame counts must be positive and q_frame0 >= 0");
-  if (p->q_frame0 + p->q_frames > p->kv_frames)
-    return fail(LCSA_ERR_INVALID, "query frames [%d, %d) are not inside the %d key frames", p->q_frame0,
-                p->q_frame0 + p->q_frames, p->kv_frames);
+  if (int64_t(p->q_frame0) + p->q_frames > p->kv_frames)  // 64-bit: the int sum could wrap
+    return fail(LCSA_ERR_INVALID, "query frames [%d, %lld) are not inside the %d key frames", p->q_frame0,
+                static_cast<long long>(p->q_frame0) + p->q_frames, p->kv_frames);
   if (p->kv_frames % kBlkT || p->q_frames % kBlkT || p->q_frame0 % kBlkT)
     return fail(LCSA_ERR_UNSUPPORTED, "frame counts and q_frame0 must be multiples of %d", kBlkT);
   if (p->win_mode < LCSA_WIN_NONE || p->win_mode > LCSA_WIN_TOKEN_PRESERVING)
@@ -69,7 +69,7 @@ lcsa_status validate_problem(const lcsa_problem* p, Geom* g) {
   const int64_t hw = static_cast<int64_t>(p->grid_h) * p->grid_w;
   const int64_t nk_tok = hw * p->kv_frames;
   // edge blocks of a grid that is not a multiple of 8 are partial (fewer rows or columns)
-  const int64_t hb_n = (p->grid_h + kBlkH - 1) / kBlkH, wb_n = (p->grid_w + kBlkW - 1) / kBlkW;
+  const int64_t hb_n = (int64_t(p->grid_h) + kBlkH - 1) / kBlkH, wb_n = (int64_t(p->grid_w) + kBlkW - 1) / kBlkW;
   const int64_t bpt = hb_n * wb_n;
   const int64_t nkb = bpt * (p->kv_frames / kBlkT);
   // every kernel indexes blocks, rows and (batch, head) pairs with 32-bit integers

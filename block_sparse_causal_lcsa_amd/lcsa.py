@@ -157,10 +157,46 @@ def _dtype(p: LcsaProblem):
     return torch.float32 if p.dtype == LCSA_F32 else torch.bfloat16
 
 
+def _on_device(name, t):
+    """Every pointer handed to the library must be device memory of the current device."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
+
+
+def _check_buffer(name, t, dtype, numel):
+    """A contiguous device tensor of `dtype` with exactly `numel` elements."""
+    _on_device(name, t)
+    if t.dtype != dtype or not t.is_contiguous() or t.numel() != numel:
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor of {numel} elements")
+
+
+_COUNTS = {}
+
+
+def _block_counts(p: LcsaProblem):
+    """(nqb, nkb, nnz_per_head) of a problem, cached by its bytes (host only)."""
+    key = bytes(p)
+    v = _COUNTS.get(key)
+    if v is None:
+        if len(_COUNTS) > 1024:
+            _COUNTS.clear()
+        v = _COUNTS[key] = lcsa_csr_layout(p)[:3]
+    return v
+
+
+def _check_selection(p, row_ptr, col_idx, nqb, nnz):
+    torch = _torch()
+    _check_buffer("row_ptr", row_ptr, torch.int32, nqb + 1)
+    if col_idx is not None:
+        _check_buffer("col_idx", col_idx, torch.int32, p.batch * p.heads * nnz)
+
+
 def _check_token_tensor(name, t, p, ntok):
     torch = _torch()
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    _on_device(name, t)
     if t.dtype != _dtype(p):
         raise ValueError(f"{name} has dtype {t.dtype}, problem expects {_dtype(p)}")
     if tuple(t.shape) != (p.batch, p.heads, ntok, p.head_dim):
@@ -171,16 +207,18 @@ def _check_token_tensor(name, t, p, ntok):
 def lcsa_pool(p: LcsaProblem, q, k, q_pooled=None, k_pooled=None, stream=None):
     """Block means of q and k (either may be None) -> (q_pooled, k_pooled) fp32 device tensors."""
     torch = _torch()
-    nqb, nkb, _, _ = lcsa_csr_layout(p)
+    nqb, nkb, _ = _block_counts(p)
     hw = p.grid_h * p.grid_w
     if q is not None:
         _check_token_tensor("q", q, p, p.q_frames * hw)
         if q_pooled is None:
             q_pooled = torch.empty((p.batch, p.heads, nqb, p.head_dim), dtype=torch.float32, device=q.device)
+        _check_buffer("q_pooled", q_pooled, torch.float32, p.batch * p.heads * nqb * p.head_dim)
     if k is not None:
         _check_token_tensor("k", k, p, p.kv_frames * hw)
         if k_pooled is None:
             k_pooled = torch.empty((p.batch, p.heads, nkb, p.head_dim), dtype=torch.float32, device=k.device)
+        _check_buffer("k_pooled", k_pooled, torch.float32, p.batch * p.heads * nkb * p.head_dim)
     zs = LcsaStrides(0, 0, 0)
     _check(load().lcsa_pool(ctypes.byref(p), _ptr(q), _strides(q) if q is not None else zs, _ptr(k),
                             _strides(k) if k is not None else zs, _ptr(q_pooled if q is not None else None),
@@ -191,17 +229,16 @@ def lcsa_pool(p: LcsaProblem, q, k, q_pooled=None, k_pooled=None, stream=None):
 def lcsa_score_select(p: LcsaProblem, q_pooled, k_pooled, row_ptr, col_idx=None, scores_dbg=None, stream=None):
     """Per-row Top-K key blocks -> col_idx int32 [B, Hh, nnz_per_head] (row_ptr: device int32)."""
     torch = _torch()
-    nqb, nkb, nnz, _ = lcsa_csr_layout(p)
+    nqb, nkb, nnz = _block_counts(p)
     for name, t, n in (("q_pooled", q_pooled, nqb), ("k_pooled", k_pooled, nkb)):
+        _on_device(name, t)
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (p.batch, p.heads, n, p.head_dim):
             raise ValueError(f"{name} must be contiguous fp32 [{p.batch}, {p.heads}, {n}, {p.head_dim}]")
-    if row_ptr.dtype != torch.int32 or row_ptr.numel() != nqb + 1 or not row_ptr.is_cuda:
-        raise ValueError("row_ptr must be a device int32 tensor of nqb + 1 entries")
     if col_idx is None:
         col_idx = torch.empty((p.batch, p.heads, nnz), dtype=torch.int32, device=q_pooled.device)
-    if scores_dbg is not None and (scores_dbg.dtype != torch.float64 or not scores_dbg.is_contiguous()
-                                   or scores_dbg.numel() != p.batch * p.heads * nqb * nkb):
-        raise ValueError("scores_dbg must be contiguous fp64 [B, Hh, nqb, nkb]")
+    _check_selection(p, row_ptr, col_idx, nqb, nnz)
+    if scores_dbg is not None:
+        _check_buffer("scores_dbg", scores_dbg, torch.float64, p.batch * p.heads * nqb * nkb)
     _check(load().lcsa_score_select(ctypes.byref(p), _ptr(q_pooled), _ptr(k_pooled), _ptr(row_ptr), _ptr(col_idx),
                                     _ptr(scores_dbg), _stream(stream)))
     return col_idx
@@ -219,8 +256,10 @@ def lcsa_attn_fwd(p: LcsaProblem, q, k, v, row_ptr, col_idx, o=None, lse=None, w
     _check_token_tensor("o", o, p, p.q_frames * hw)
     if lse is None and want_lse:
         lse = torch.empty((p.batch, p.heads, p.q_frames * hw), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be contiguous fp32 [B, Hh, Nq]")
+    if lse is not None:
+        _check_buffer("lse", lse, torch.float32, p.batch * p.heads * p.q_frames * hw)
+    nqb, _, nnz = _block_counts(p)
+    _check_selection(p, row_ptr, col_idx, nqb, nnz)
     _check(load().lcsa_attn_fwd(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                 _ptr(row_ptr), _ptr(col_idx), _ptr(o), _strides(o), _ptr(lse), _stream(stream)))
     return o, lse
@@ -241,18 +280,25 @@ def lcsa_attn_bwd(p: LcsaProblem, q, k, v, o, d_o, lse, row_ptr, col_idx, dq=Non
     nq, nk = p.q_frames * hw, p.kv_frames * hw
     for name, t, n in (("q", q, nq), ("k", k, nk), ("v", v, nk), ("o", o, nq), ("d_o", d_o, nq)):
         _check_token_tensor(name, t, p, n)
-    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != p.batch * p.heads * nq:
-        raise ValueError("lse must be contiguous fp32 [B, Hh, Nq] (the forward's output)")
+    if lse is None:
+        raise ValueError("lse (the forward's output) is required")
+    _check_buffer("lse", lse, torch.float32, p.batch * p.heads * nq)
+    nqb, _, nnz = _block_counts(p)
+    _check_selection(p, row_ptr, col_idx, nqb, nnz)
     grads = []
     for name, t, n in (("dq", dq, nq), ("dk", dk, nk), ("dv", dv, nk)):
         if t is None:
             t = torch.empty((p.batch, p.heads, n, p.head_dim), dtype=torch.float32, device=q.device)
+        _on_device(name, t)
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (p.batch, p.heads, n, p.head_dim):
             raise ValueError(f"{name} must be contiguous fp32 [{p.batch}, {p.heads}, {n}, {p.head_dim}]")
         grads.append(t)
     need = lcsa_attn_bwd_workspace_size(p)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _on_device("workspace", workspace)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
     _check(load().lcsa_attn_bwd(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                 _ptr(o), _strides(o), _ptr(d_o), _strides(d_o), _ptr(lse), _ptr(row_ptr),
                                 _ptr(col_idx), _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]), _ptr(workspace),
@@ -364,6 +410,7 @@ def lcsa_rope_qkv(p: LcsaProblem, rope: LcsaRope, qkv, frame0: int, q=None, k=No
     if qkv.dim() != 3 or qkv.dtype != torch.bfloat16 or qkv.stride(2) != 1 or qkv.shape[0] != p.batch \
             or qkv.shape[2] != 3 * p.heads * p.head_dim or qkv.shape[1] % hw:
         raise ValueError("qkv must be bf16 [B, frames*H*W, 3*heads*head_dim] with unit last stride")
+    _on_device("qkv", qkv)
     n = qkv.shape[1]
     outs = []
     for name, t in (("q", q), ("k", k), ("v", v)):

@@ -101,6 +101,10 @@ BASE = W.CHUNK_768
     (dict(win_mode=2, win_h=0, win_w=72), lcsa.LCSA_ERR_INVALID),
     (dict(win_mode=5, win_h=72, win_w=72), lcsa.LCSA_ERR_INVALID),
     (dict(win_mode=3, win_h=0, win_w=72), lcsa.LCSA_ERR_INVALID),
+    # sums that would wrap in 32-bit arithmetic
+    (dict(q_frame0=2**31 - 2, q_frames=2), lcsa.LCSA_ERR_INVALID),
+    (dict(grid_h=2**31 - 1), lcsa.LCSA_ERR_UNSUPPORTED),
+    (dict(grid_h=2**16, grid_w=2**16), lcsa.LCSA_ERR_UNSUPPORTED),
 ])
 def test_invalid_problems_rejected_on_host(change, status):
     _check_rejected(BASE.replace(**change), status)
@@ -296,3 +300,27 @@ def test_rope_struct_layout_matches_header(tmp_path):
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
     assert got[:-1] == [getattr(lcsa.LcsaRope, f).offset for f in fields]
     assert got[-1] == ctypes.sizeof(lcsa.LcsaRope)
+
+
+def test_binding_rejects_host_tensors():
+    """Host (CPU) tensors never reach the library: each call raises before any device work."""
+    import torch
+    w = W.Workload("host_check", 1, 2, 64, 16, 16, 4, 2, 2)
+    p = lcsa.problem(w)
+    nq, nk = 2 * 16 * 16, 4 * 16 * 16
+    q = torch.zeros((1, 2, nq, 64), dtype=torch.bfloat16)
+    k = torch.zeros((1, 2, nk, 64), dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    nqb, nkb, nnz, rp = lcsa.lcsa_csr_layout(p)
+    row_ptr = torch.from_numpy(rp)
+    col = torch.zeros((1, 2, nnz), dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        lcsa.lcsa_pool(p, q, k)
+    with pytest.raises(ValueError, match="device tensor"):
+        lcsa.lcsa_score_select(p, torch.zeros((1, 2, nqb, 64)), torch.zeros((1, 2, nkb, 64)), row_ptr)
+    with pytest.raises(ValueError, match="device tensor"):
+        lcsa.lcsa_attn_fwd(p, q, k, v, row_ptr, col)
+    with pytest.raises(ValueError, match="device tensor"):
+        lcsa.lcsa_attn_bwd(p, q, k, v, q, q, torch.zeros((1, 2, nq)), row_ptr, col)
+    with pytest.raises(ValueError, match="device tensor"):
+        lcsa.lcsa_rope_qkv(p, lcsa.LcsaRope(22, 20, 22, 10000.0), torch.zeros((1, nq, 3 * 2 * 64), dtype=torch.bfloat16), 2)

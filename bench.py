@@ -27,7 +27,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 CSRC = os.path.join(ROOT, "block_sparse_causal_lcsa_amd", "csrc")
 # the sources of the attention kernel whose HBM traffic the committed counter summary records
-KERNEL_SRCS = ["attn_fwd_impl.h", "attn_fwd_dense.hip", "attn_fwd.hip"]
+KERNEL_SRCS = ["attn_fwd_impl.h", "attn_fwd_block.hip", "attn_fwd.hip"]
 
 
 def kernel_hash() -> str:

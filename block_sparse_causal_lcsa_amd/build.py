@@ -16,17 +16,17 @@ OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblcsa.so")
 ARCH = "gfx950"
 
-KERNELS = ["pool.hip", "score_select.hip", "attn_fwd.hip", "attn_fwd_dense.hip", "attn_bwd.hip", "stream.hip",
+KERNELS = ["pool.hip", "score_select.hip", "attn_fwd.hip", "attn_fwd_block.hip", "attn_bwd.hip", "stream.hip",
            "rope.hip"]
 HOST = ["lcsa_host.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 # Packed fp32 VALU ops are kept out of every device build.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
-# Per-unit extra flags. The unmasked attention kernel runs 7% faster under the iterative ILP machine
-# scheduler (LDS operand reads spread between the MFMAs); the other units are no faster with it, and
-# the masked attention variants spill more registers.
-EXTRA = {"attn_fwd_dense.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+# Per-unit extra flags. The block-granular attention variants run 7% faster under the iterative ILP
+# machine scheduler (LDS operand reads spread between the MFMAs); the other units are no faster with
+# it, and the token-window attention variant spills more registers.
+EXTRA = {"attn_fwd_block.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _run(cmd):

@@ -1,7 +1,7 @@
 // lcsa_attn_fwd: exact softmax attention of each 128-token query block over the tokens of its kept
 // key blocks (FlashVSR summary, sec. 2.2: full attention is applied inside the selected blocks only).
-// The kernels are in attn_fwd_impl.h; this unit validates the call and launches the masked bf16
-// variants and the fp32 kernel, attn_fwd_dense.hip the unmasked bf16 kernel.
+// The kernels are in attn_fwd_impl.h; this unit validates the call and launches the token-window bf16
+// variant and the fp32 kernel, attn_fwd_block.hip the block-granular bf16 variants.
 #include "attn_fwd_impl.h"
 
 using namespace lcsa;
@@ -50,14 +50,11 @@ extern "C" lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_
     a.nwg = (a.nrows + 1) / 2;  // two query blocks per workgroup
     const bool ragged = (g.H % kBlkH) != 0 || (g.W % kBlkW) != 0;
     const int mask = token_window(g) ? kMaskWindow : (ragged ? kMaskRagged : kMaskNone);
-    if (p->head_dim == 128) {
-      if (mask == kMaskWindow) attn_fwd_pp_kernel<128, kMaskWindow><<<a.nwg, 512, 0, s>>>(a);
-      else if (mask == kMaskRagged) attn_fwd_pp_kernel<128, kMaskRagged><<<a.nwg, 512, 0, s>>>(a);
-      else launch_attn_fwd_pp_dense(a, 128, s);
+    if (mask == kMaskWindow) {
+      if (p->head_dim == 128) attn_fwd_pp_kernel<128, kMaskWindow><<<a.nwg, 512, 0, s>>>(a);
+      else attn_fwd_pp_kernel<64, kMaskWindow><<<a.nwg, 512, 0, s>>>(a);
     } else {
-      if (mask == kMaskWindow) attn_fwd_pp_kernel<64, kMaskWindow><<<a.nwg, 512, 0, s>>>(a);
-      else if (mask == kMaskRagged) attn_fwd_pp_kernel<64, kMaskRagged><<<a.nwg, 512, 0, s>>>(a);
-      else launch_attn_fwd_pp_dense(a, 64, s);
+      launch_attn_fwd_pp_block(a, p->head_dim, mask == kMaskRagged, s);
     }
   } else {
     if (p->head_dim == 128) attn_fwd_kernel<float, 128><<<a.nwg, 256, 0, s>>>(a);

@@ -1,4 +1,4 @@
-// Device code of lcsa_attn_fwd (attn_fwd.hip, attn_fwd_dense.hip): exact softmax attention of each
+// Device code of lcsa_attn_fwd (attn_fwd.hip, attn_fwd_block.hip): exact softmax attention of each
 // 128-token query block over the tokens of its kept key blocks (FlashVSR summary, sec. 2.2: full
 // attention is applied inside the selected blocks only).
 //
@@ -48,9 +48,10 @@ struct AttnArgs {
   int32_t nrows;            // (batch, head, query block) rows = B * Hh * nqb
 };
 
-// Launches the bf16 ping-pong kernel for grids of whole blocks with no token mask (head_dim 64 or
-// 128); defined in its own translation unit, which is compiled with a different instruction scheduler.
-void launch_attn_fwd_pp_dense(const AttnArgs& a, int head_dim, hipStream_t s);
+// Launches the bf16 ping-pong kernel for block-granular masks (whole blocks, or partial edge blocks
+// when `ragged`; head_dim 64 or 128); defined in attn_fwd_block.hip, which is compiled with a
+// different instruction scheduler.
+void launch_attn_fwd_pp_block(const AttnArgs& a, int head_dim, bool ragged, hipStream_t s);
 
 namespace {
 

@@ -392,7 +392,6 @@ constexpr int kSub = 64;  // keys per sub-block
 // Bound on a lane's sum of 32 unnormalised probabilities before the running maximum is refreshed:
 // every P stays below 2^16, far from overflowing the fp32 accumulators for finite inputs.
 constexpr float kSumMax = 65536.0f;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct Tile {
@@ -653,16 +652,13 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[kt][h2][e] = (__bf16)x[kt][8 * h2 + e];
-    // row sum of the rounded probabilities that P V uses: bf16 pair dot products with (1, 1)
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // row sum of the fp32 probabilities, before their rounding to bf16: the denominator (and lse)
+    // stay exact to fp32 even when one rounded probability carries most of a row's mass
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 8; e += 2)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 w = pf[u >> 1][u & 1];
-        acc[u] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[e], w[e + 1]}, ones, acc[u], false);
-      }
+      for (int v = 0; v < 16; ++v) acc[v & 3] += x[kt][v];
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
   auto vphase = [&](bool ok, int lim) __attribute__((always_inline)) {

@@ -12,12 +12,12 @@ Tolerances (fixed here, used by every GPU test):
               be identical, position by position.
   output      attention is recomputed by the oracle on the kept set the GPU chose (validated above)
               so the error measures attention only: max |O - O_ref| <= 2e-2 and
-              mean |O - O_ref| <= 2e-3 at bf16 I/O; lse max abs <= 1e-3 for bf16 inputs, 1e-2 for
-              fp32 inputs (the kernel rounds Q/K to bf16 on load), and sum_k exp(l - lse_gpu) = 1
-              within the same bound per row (|sum - 1| is about |lse error|). A row that sees fewer
-              than 128 keys (token-granular windows) gets max(that bound, 2^-8): its denominator sums
-              few bf16-rounded probabilities, each within 2^-8 of its value, with little averaging.
-              A row that sees none of its kept keys must have O = 0 and lse = -inf exactly.
+              mean |O - O_ref| <= 2e-3 at bf16 I/O; lse max abs <= 1e-4 for bf16 inputs (the
+              kernel sums the fp32 probabilities, so lse carries fp32 rounding only: ~2e-6
+              measured), 1e-2 for fp32 inputs (the kernel rounds Q/K to bf16 on load), and
+              sum_k exp(l - lse_gpu) = 1 within twice that bound per row (|sum - 1| is about
+              |lse error|). A row that sees none of its kept keys must have O = 0 and lse = -inf
+              exactly.
 """
 from __future__ import annotations
 
@@ -29,6 +29,7 @@ from oracle import lcsa_oracle as O
 
 NEAR_TIE = 1e-5
 O_MAX, O_MEAN = 2e-2, 2e-3
+LSE_BF16, LSE_F32 = 1e-4, 1e-2
 
 
 def to_device(x: np.ndarray, device="cuda"):
@@ -112,25 +113,6 @@ def check_selection(w, gpu, ref_scores, ref_col, row_ptr):
     return near, swapped
 
 
-def visible_key_counts(w, gpu, qblocks=None, bh=None):
-    """[B, Hh, Nq]: how many tokens of its kept blocks each query token sees (token windows, partial
-    blocks); -1 where not computed."""
-    qb, kb = O.query_blocks(w), O.key_blocks(w)
-    B, Hh = gpu["col_idx"].shape[:2]
-    out = np.full((B, Hh, w.q_frames * w.grid_h * w.grid_w), -1, dtype=np.int64)
-    qblocks = range(len(qb)) if qblocks is None else qblocks
-    bh = [(b, h) for b in range(B) for h in range(Hh)] if bh is None else bh
-    ktok = [O.block_tokens(w, blk, 0) for blk in kb]
-    rp = gpu["row_ptr"]
-    for i in qblocks:
-        qt = O.block_tokens(w, qb[i], w.q_frame0)
-        for b, h in bh:
-            sel = gpu["col_idx"][b, h, rp[i]:rp[i + 1]]
-            kt = np.concatenate([ktok[j] for j in sel])
-            out[b, h, qt] = O.token_pair_mask(w, qt, kt).sum(axis=1)
-    return out
-
-
 def check_attention(w, x64, gpu, qblocks=None, bh=None):
     """Oracle attention on the GPU's kept sets for the given rows; returns error stats."""
     q, k, v = x64
@@ -148,14 +130,11 @@ def check_attention(w, x64, gpu, qblocks=None, bh=None):
                  blind_rows=int(blind.sum()))
     assert stats["o_max"] <= O_MAX, stats
     assert stats["o_mean"] <= O_MEAN, stats
-    lse_tol = 1e-3 if w.dtype == "bf16" else 1e-2
-    # The denominator sums the bf16-rounded probabilities (those P V uses): each is within 2^-8 of its
-    # value, so lse is within about 2^-8 of the exact one whatever the count; over many keys the
-    # roundings average out and 1e-3 holds. Rows that see fewer than 128 keys (token windows) get 2^-8.
-    few = rows & (visible_key_counts(w, gpu, qblocks, bh) < 128)
-    stats["few_key_rows"] = int(few.sum())
-    assert np.all(np.abs(lg[rows & ~few] - lref[rows & ~few]) <= lse_tol), stats
-    assert np.all(np.abs(lg[few] - lref[few]) <= max(lse_tol, 2.0 ** -8)), stats
+    # The denominator sums the fp32 probabilities before their rounding to bf16, so at bf16 I/O lse
+    # carries only the fp32 rounding of the scores and sums (about 2e-6 at these sizes); fp32 I/O
+    # rounds Q and K to bf16 on load, which moves the scores themselves.
+    lse_tol = LSE_BF16 if w.dtype == "bf16" else LSE_F32
+    assert stats["lse_max"] <= lse_tol, stats
     # softmax normalisation with the GPU's lse, for a few rows
     qb, kb = O.query_blocks(w), O.key_blocks(w)
     qblocks = list(range(len(qb))) if qblocks is None else list(qblocks)
@@ -166,8 +145,7 @@ def check_attention(w, x64, gpu, qblocks=None, bh=None):
         l = np.where(O.token_pair_mask(w, qt, kt), w.scale * q[b, h, qt] @ k[b, h, kt].T, -np.inf)
         seen = np.isfinite(lg[b, h, qt])
         sums = np.exp(l[seen] - lg[b, h, qt][seen][:, None]).sum(axis=1)
-        tol = np.where(np.isfinite(l[seen]).sum(axis=1) < 128, max(lse_tol, 2.0 ** -8), lse_tol)
-        assert np.all(np.abs(sums - 1.0) <= tol), sums
+        assert np.all(np.abs(sums - 1.0) <= 2 * lse_tol), sums
     return stats
 
 

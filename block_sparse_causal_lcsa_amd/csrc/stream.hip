@@ -73,6 +73,8 @@ struct CopyArgs {
   int64_t ring_head;
   int64_t dst_tok0;   // first destination token in the ring
   int32_t heads, cpt;
+  int32_t lcpt;       // log2(cpt): cpt = head_dim * element size / 16 is 8, 16 or 32
+  int64_t bh_n;       // B * Hh
   int64_t n_tok;
   int64_t n;          // B * Hh * n_tok * cpt
 };
@@ -85,25 +87,40 @@ struct ShiftArgs {
   int64_t n;          // B * Hh * keep_rows * vpr
 };
 
+// K/V copy: blockIdx.x tiles the tokens (256 / cpt per workgroup), blockIdx.y walks the (batch,
+// head) pairs, so a lane's token and 16-byte chunk come from shifts and no division runs per chunk.
+// The pooled-K shift is a grid-stride loop over the whole grid.
 __global__ __launch_bounds__(256) void stream_copy_kernel(CopyArgs c, ShiftArgs s) {
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < c.n; e += stride) {
-    const int64_t ch = e % c.cpt, tok = (e / c.cpt) % c.n_tok, bh = e / (int64_t(c.cpt) * c.n_tok);
-    const int64_t b = bh / c.heads, h = bh - (bh / c.heads) * c.heads;
-    const int64_t dst = bh * c.ring_head + (c.dst_tok0 + tok) * c.cpt + ch;
-    c.k_dst[dst] = c.k_src[b * c.ksb + h * c.ksh + tok * c.kst + ch];
-    c.v_dst[dst] = c.v_src[b * c.vsb + h * c.vsh + tok * c.vst + ch];
+  if (c.n > 0) {
+    const int64_t tok = int64_t(blockIdx.x) * (256 >> c.lcpt) + (threadIdx.x >> c.lcpt);
+    const int64_t ch = threadIdx.x & ((1 << c.lcpt) - 1);
+    if (tok < c.n_tok) {
+      for (int64_t bh = blockIdx.y; bh < c.bh_n; bh += gridDim.y) {
+        const int64_t b = bh / c.heads, h = bh - b * c.heads;
+        const int64_t dst = bh * c.ring_head + ((c.dst_tok0 + tok) << c.lcpt) + ch;
+        c.k_dst[dst] = c.k_src[b * c.ksb + h * c.ksh + tok * c.kst + ch];
+        c.v_dst[dst] = c.v_src[b * c.vsb + h * c.vsh + tok * c.vst + ch];
+      }
+    }
   }
-  for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < s.n; e += stride) {
+  const int64_t stride = int64_t(gridDim.x) * gridDim.y * blockDim.x;
+  for (int64_t e = (int64_t(blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; e < s.n; e += stride) {
     const int64_t ch = e % s.vpr, r = (e / s.vpr) % s.keep_rows, bh = e / (int64_t(s.vpr) * s.keep_rows);
     s.new_buf[(bh * s.new_rows + r) * s.vpr + ch] = s.old_buf[(bh * s.old_rows + r + s.shift_rows) * s.vpr + ch];
   }
 }
 
 lcsa_status launch_copy(const CopyArgs& c, const ShiftArgs& s, hipStream_t hs, const char* what) {
-  const int64_t work = c.n > s.n ? c.n : s.n;
-  if (work == 0) return LCSA_OK;
-  const int grid = static_cast<int>((work + 255) / 256 < 8192 ? (work + 255) / 256 : 8192);
+  if (c.n == 0 && s.n == 0) return LCSA_OK;
+  dim3 grid(1, 1);
+  if (c.n > 0) {
+    if (c.cpt != (1 << c.lcpt) || c.lcpt < 3 || c.lcpt > 5) return fail(LCSA_ERR_UNSUPPORTED, "%s: chunk count", what);
+    const int64_t tpb = 256 >> c.lcpt;
+    grid.x = static_cast<uint32_t>((c.n_tok + tpb - 1) / tpb);
+    grid.y = static_cast<uint32_t>(c.bh_n < 65535 ? c.bh_n : 65535);
+  } else {
+    grid.x = static_cast<uint32_t>((s.n + 255) / 256 < 8192 ? (s.n + 255) / 256 : 8192);
+  }
   (void)hipGetLastError();
   stream_copy_kernel<<<grid, 256, 0, hs>>>(c, s);
   return hip_status(hipGetLastError(), what);
@@ -144,6 +161,8 @@ lcsa_status make_room(lcsa_stream* s, const lcsa_problem& w1, const StreamLayout
     c.dst_tok0 = 0;
     c.heads = w1.heads;
     c.cpt = static_cast<int32_t>(cpt);
+    c.lcpt = __builtin_ctz(static_cast<unsigned>(cpt));
+    c.bh_n = int64_t(w1.batch) * w1.heads;
     c.n_tok = int64_t(keep) * l.tb_tokens;
     c.n = int64_t(w1.batch) * w1.heads * c.n_tok * cpt;
     ShiftArgs none{};
@@ -248,6 +267,8 @@ extern "C" lcsa_status lcsa_stream_push(lcsa_stream* s, const void* k_new, lcsa_
     c.dst_tok0 = int64_t(s->wpos) * l.tb_tokens;
     c.heads = w1.heads;
     c.cpt = w1.head_dim / epc;
+    c.lcpt = __builtin_ctz(static_cast<unsigned>(c.cpt));
+    c.bh_n = bh;
     c.n_tok = l.tb_tokens;
     c.n = bh * l.tb_tokens * c.cpt;
   }

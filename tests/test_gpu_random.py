@@ -75,3 +75,44 @@ def test_random_backward(w):
             assert not np.any(r[n]), f"{n}: oracle gradient is zero, GPU's is not"
     stats["unkept_key_blocks"] = check_unkept_zero(w, r)
     report(w.name, stats)
+
+
+def random_streams(n, seed):
+    """(sequence workload, cache blocks, ring blocks, chunks pushed in place) per random stream."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for idx in range(n):
+        H, Wd = int(rng.integers(3, 33)), int(rng.integers(3, 41))
+        nchunks = int(rng.integers(2, 9))
+        cache = int(rng.integers(1, 5))
+        ring = 0 if idx % 2 == 0 else 2 * cache - 1 + int(rng.integers(0, 4))
+        mode = int(rng.integers(0, 5))
+        if mode in (1, 2):
+            win_h, win_w = 8 * (2 * int(rng.integers(0, 3)) + 1), 8 * (2 * int(rng.integers(0, 3)) + 1)
+        elif mode in (3, 4):
+            win_h, win_w = int(rng.integers(1, 2 * H + 2)), int(rng.integers(1, 2 * Wd + 2))
+        else:
+            win_h = win_w = 0
+        topk = int(rng.choice([0, 0, 1, 3]))
+        rho = float(rng.choice([0.1, 0.3, 0.6, 1.0]))
+        dtype = "f32" if idx % 4 == 3 else "bf16"
+        d = int(rng.choice([64, 128]))
+        batch, heads = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        in_place = tuple(int(c) for c in rng.choice(nchunks, size=min(2, nchunks), replace=False))
+        name = (f"rstream{idx}_{batch}x{heads}_d{d}_{dtype}_{H}x{Wd}_c{cache}r{ring}_n{nchunks}_w{mode}"
+                f"-{win_h}x{win_w}_k{topk or rho}")
+        seq = W.Workload(name, batch, heads, d, H, Wd, 2 * nchunks, 0, 2 * nchunks, dtype=dtype, win_mode=mode,
+                         win_h=win_h, win_w=win_w, topk=topk, keep_ratio=rho)
+        out.append((seq, cache, ring, in_place))
+    return out
+
+
+STREAMS = random_streams(8, 77)
+
+
+@pytest.mark.parametrize("case", STREAMS, ids=lambda c: c[0].name)
+def test_random_stream(case):
+    from test_gpu_stream import run_stream
+    seq, cache, ring, in_place = case
+    nchunks = seq.kv_frames // 2
+    run_stream(seq, cache, seed=5, oracle_chunks=(0, nchunks - 1), ring=ring, in_place=in_place)

@@ -193,3 +193,27 @@ def test_backward_chunk_768x1408_sampled():
         stats[f"dv_h{h}"] = compare("dv", r["dv"], dV, m)
     stats["unkept_key_blocks"] = check_unkept_zero(w, r)
     report(w.name, stats)
+
+
+def test_backward_strided_inputs_match_contiguous():
+    """Q, K, V, O and dO as [B, tokens, heads, d] storage viewed as [B, heads, tokens, d] (token
+    stride heads*d): the gradients equal those of contiguous copies bit for bit."""
+    w = W.Workload("bwd_strided", 2, 3, 128, 16, 24, 4, 2, 2, keep_ratio=0.5)
+    p = lcsa.problem(w)
+    x = inputs.make_inputs(w, 6)
+    g = inputs.make_grad(w, 6)
+    q, k, v, d_o = (to_device(a) for a in (x["q"], x["k"], x["v"], g))
+    out = lcsa.forward(p, q, k, v)
+    args = (out["row_ptr"], out["col_idx"])
+    ref = lcsa.lcsa_attn_bwd(p, q, k, v, out["o"], d_o, out["lse"], *args)
+
+    def strided(t):
+        s = t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        assert s.stride(2) == w.heads * w.head_dim and torch.equal(s, t)
+        return s
+
+    got = lcsa.lcsa_attn_bwd(p, strided(q), strided(k), strided(v), strided(out["o"]), strided(d_o), out["lse"],
+                             *args)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(a, b), name

@@ -79,8 +79,8 @@ def main():
                          "of 256 MiB (the byte-counter calibration kernel); prints a short line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the LCSA forward here runs on a single MI355X; "
-              "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU: the LCSA forward here runs on a single MI355X, and "
+              "sharding over several GPUs is not implemented (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -14,7 +14,7 @@ fmread pdfshare summary of the paper:
   * sec. 2.3, locality-constrained attention: at inference each query's attention is confined to a
     local spatial neighbourhood (1152x1152 px in the example), with a "boundary-truncated" and a
     "boundary-preserving" rule compared in sec. 3 (ablation, locality-constrained attention).
-The passages leave several steps open; the readings taken here (all stated in the design doc) are:
+The passages leave several steps open; the readings taken here are:
   R1 causality is block-causal: key block j is visible from query block i iff its temporal block
      index (latent frame // 2) is <= that of i; a block is fully visible inside the current one.
   R2 Top-K is taken per query block over its visible key blocks, independently per (batch, head).

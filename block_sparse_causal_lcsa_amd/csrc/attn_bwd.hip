@@ -448,7 +448,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) uint16_t qbuf[2 * TE];
   __shared__ __attribute__((aligned(16))) uint16_t gbuf[2 * TE];
   __shared__ __attribute__((aligned(16))) float rlbuf[2 * 2 * kTok];   // per stage: [lse2 | delta]
-  __shared__ __attribute__((aligned(16))) float pbuf[4 * 2 * 16 * 64];  // per key tile: P, [t][v][lane]
+  // per key tile: P as [lane][kPRow] floats, items (t, v) at t * 16 + v; the padded row makes the
+  // 16-byte accesses of 16 consecutive lanes cover all 64 banks once
+  constexpr int kPRow = 36;
+  __shared__ __attribute__((aligned(16))) float pbuf[4 * 64 * kPRow];
   const Geom& g = a.g;
   const int bh = xcd_order() / g.nkb, j = xcd_order() - bh * g.nkb;
   const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const const_i32* cp = (const const_i32*)(a.col_ptr) + int64_t(bh) * (g.nkb + 1);
   const int beg = cp[j], nrow = cp[j + 1] - beg;
   const const_i32* rows = (const const_i32*)(a.row_of) + int64_t(bh) * a.nnz + beg;
-  float* pmine = pbuf + kr * (2 * 16 * 64);
+  float* pmine = pbuf + kr * (64 * kPRow) + lane * kPRow;
 
   f32x16 acc[DT];  // dV^T (role 0) or dK^T (role 1)
 #pragma unroll
@@ -582,7 +585,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
         }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) pmine[(t * 16 + v) * 64 + lane] = pv[v];
+        for (int v4 = 0; v4 < 4; ++v4)
+          *reinterpret_cast<float4*>(pmine + t * 16 + 4 * v4) =
+              make_float4(pv[4 * v4], pv[4 * v4 + 1], pv[4 * v4 + 2], pv[4 * v4 + 3]);
         pack_b(pv, bop[t]);
       }
       tile_barrier();    // P published
@@ -596,11 +601,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float4 d4 = *reinterpret_cast<const float4*>(rl + kTok + t * 32 + g4 * 8 + 4 * hi);
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+          const float4 p4 = *reinterpret_cast<const float4*>(pmine + t * 16 + 4 * g4);
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w}, pv4[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * g4 + e;
-            ds[v] = pmine[(t * 16 + v) * 64 + lane] * (x[t][v] - dv4[e]);
+            ds[v] = pv4[e] * (x[t][v] - dv4[e]);
           }
         }
         pack_b(ds, bop[t]);

@@ -120,8 +120,9 @@ lcsa_status lcsa_score_select(const lcsa_problem* p, const float* q_pooled, cons
  * q: [B, Hh, Nq, d]; k, v: [B, Hh, Nk, d]; o: [B, Hh, Nq, d], all of the problem's dtype.
  * lse: NULL, or device fp32 [B, Hh, Nq] contiguous: natural log of the softmax denominator.
  * Arithmetic: bf16 inputs as given (fp32 inputs are rounded to bf16 on load), bf16 MFMA with fp32
- * accumulation for QK^T and PV, online softmax in fp32, P rounded to bf16; O written as bf16 (RNE)
- * or fp32. col_idx entries outside [0, nkb) are skipped. */
+ * accumulation for QK^T and PV, online softmax in fp32, P rounded to bf16 for PV while the
+ * denominator (and lse) sums the fp32 P; O written as bf16 (RNE) or fp32. col_idx entries outside
+ * [0, nkb) are skipped. */
 lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
                           lcsa_strides ks, const void* v, lcsa_strides vs, const int32_t* row_ptr,
                           const int32_t* col_idx, void* o, lcsa_strides os, float* lse,

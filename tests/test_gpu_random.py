@@ -50,7 +50,7 @@ def random_problems(n, seed):
     return out
 
 
-PROBLEMS = random_problems(16, 2024)
+PROBLEMS = random_problems(16, 2024) + [w.replace(name=w.name.replace("rand", "rnd")) for w in random_problems(24, 99)]
 
 
 @pytest.mark.parametrize("w", PROBLEMS, ids=lambda w: w.name)

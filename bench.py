@@ -52,12 +52,50 @@ def traffic_from_profile(workload: str):
     return float(t.group(1))
 
 
+def settle(run, seconds: float) -> float:
+    """Untimed steps until at least `seconds` of wall time have passed (synchronising every 10 steps),
+    so that clocks and caches reach their steady state whatever --warmup says. Returns the time spent."""
+    import torch
+
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(10):
+            run()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            return dt
+
+
+def pct(a, q: float) -> float:
+    import numpy as np
+    return round(float(np.percentile(np.asarray(a, dtype=np.float64), q)), 4)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="chunk_768x1408_q2_kv6")
+    ap.add_argument("--settle", type=float, default=1.5, metavar="SECONDS",
+                    help="untimed steps for at least this wall time after the warmup steps, before any "
+                         "timing (reported as settle_s)")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="repetitions of the cold-cache leg: pool and score_select each timed right after "
+                         "a 1 GiB device write that evicts L2 and the Infinity Cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=0,
                     help="query blocks per head in the oracle sample (0 = all)")
@@ -143,6 +181,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    settle_s = settle(step, args.settle)
 
     # optionally, one step captured as a HIP graph and replayed
     run_step = step
@@ -204,6 +243,29 @@ def main():
     achieved = flop / (attn_ms * 1e-3) / 1e12
     traffic = traffic_from_profile(w.name)
 
+    # cold-cache leg: each pool and each score_select is timed right after a read sweep over a 1 GiB
+    # buffer (written once, before the leg), which evicts the 4 MB L2s and the 256 MB Infinity Cache
+    # without leaving dirty lines whose write-back would share HBM with the timed kernel; the bytes
+    # the timed kernel reads come from HBM
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    cold_pool, cold_sel = [], []
+    stream = torch.cuda.current_stream()
+    for _ in range(args.cold_reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        flush.sum()
+        e[0].record(stream)
+        lcsa.lcsa_pool(p, q, k, qp, kp, stream=stream)
+        e[1].record(stream)
+        flush.sum()
+        e[2].record(stream)
+        lcsa.lcsa_score_select(p, qp, kp, row_ptr, col, stream=stream)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        cold_pool.append(e[0].elapsed_time(e[1]))
+        cold_sel.append(e[2].elapsed_time(e[3]))
+    del flush
+
     out = {
         "metric": "LCSA fwd effective TFLOP/s on selected blocks + ms per 8-frame chunk",
         "value": round(flop / (ms_per_step * 1e-3) / 1e12, 2),
@@ -224,10 +286,21 @@ def main():
                    "selected_pairs": pairs, "selected_gflop": round(flop / 1e9, 2)},
         "ms_per_chunk": round(ms_per_step, 4),
         "launch": "eager" if run_step is step else "hip_graph",
+        "settle_s": round(settle_s, 2),
         "kernels_ms_median": {"lcsa_pool": round(med(t_pool), 4), "lcsa_score_select": round(med(t_sel), 4),
                               "lcsa_attn_fwd": round(med(t_attn), 4), "step_events": round(med(t_step_ev), 4)},
+        "kernels_ms_p10": {"lcsa_pool": pct(t_pool, 10), "lcsa_score_select": pct(t_sel, 10),
+                           "lcsa_attn_fwd": pct(t_attn, 10), "step_events": pct(t_step_ev, 10)},
+        "kernels_ms_p90": {"lcsa_pool": pct(t_pool, 90), "lcsa_score_select": pct(t_sel, 90),
+                           "lcsa_attn_fwd": pct(t_attn, 90), "step_events": pct(t_step_ev, 90)},
         "pool_gbs": round(pool_bytes / (med(t_pool) * 1e-3) / 1e9, 1),
         "score_select_gbs": round(sel_bytes / (med(t_sel) * 1e-3) / 1e9, 1),
+        "cold_cache": {"flush": "read sweep of 1 GiB before each timed call", "reps": args.cold_reps,
+                       "lcsa_pool_ms_median": round(med(cold_pool), 4),
+                       "lcsa_score_select_ms_median": round(med(cold_sel), 4),
+                       "pool_gbs_cold": round(pool_bytes / (med(cold_pool) * 1e-3) / 1e9, 1),
+                       "pool_frac_of_hbm_peak": round(pool_bytes / (med(cold_pool) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "score_select_gbs_cold": round(sel_bytes / (med(cold_sel) * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "kernel": "lcsa_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "flop_per_launch": flop, "avg_launch_ms": round(attn_ms, 4),
@@ -265,6 +338,7 @@ def backward_bench(args, w, p, x, dev, step, t):
     for _ in range(args.warmup):
         bwd()
     torch.cuda.synchronize()
+    settle_s = settle(bwd, args.settle)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         bwd()
@@ -277,7 +351,8 @@ def backward_bench(args, w, p, x, dev, step, t):
         bwd()
         e1.record(stream)
     torch.cuda.synchronize()
-    call_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    call_t = [e0.elapsed_time(e1) for e0, e1 in evs]
+    call_ms = float(np.mean(call_t))
     pairs = w.batch * w.heads * t["nnz"]
     flop = pairs * 10.0 * 128 * 128 * w.head_dim
     executed = pairs * 14.0 * 128 * 128 * w.head_dim
@@ -287,6 +362,8 @@ def backward_bench(args, w, p, x, dev, step, t):
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: the forward's inputs; dO ~ N(0,1) rounded to bf16",
+        "settle_s": round(settle_s, 2),
+        "call_ms": {"p10": pct(call_t, 10), "median": pct(call_t, 50), "p90": pct(call_t, 90)},
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "grid": [w.grid_h, w.grid_w], "selected_pairs": pairs},
         "roofline": {"bound": "mfma", "kernel": "lcsa_attn_bwd (delta, csc, dq, dkdv launches)",
@@ -338,6 +415,13 @@ def stream_bench(args, w):
         one(c)
         c += 1
     torch.cuda.synchronize()
+
+    def one_next():
+        nonlocal c
+        one(c)
+        c += 1
+
+    settle_s = settle(one_next, args.settle)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         out = one(c)
@@ -359,6 +443,7 @@ def stream_bench(args, w):
         "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic: seeded smooth sinusoidal Q/K fields + 0.5 N(0,1), V ~ N(0,1)",
+        "settle_s": round(settle_s, 2),
         "config": {"workload": f"{w.name} streamed, cache {args.stream} temporal blocks", "heads": w.heads,
                    "head_dim": w.head_dim, "grid": [w.grid_h, w.grid_w], "window_kv_frames": pw.kv_frames},
         "kernels_ms_median": {"lcsa_stream_push": round(push_ms, 4), "pool_select_attn": round(fwd_ms, 4)},
@@ -389,6 +474,13 @@ def layer_bench(args, w):
         layer.step(xs[c % 4])
         c += 1
     torch.cuda.synchronize()
+
+    def one_next():
+        nonlocal c
+        layer.step(xs[c % 4])
+        c += 1
+
+    settle_s = settle(one_next, args.settle)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         layer.step(xs[c % 4])
@@ -410,7 +502,7 @@ def layer_bench(args, w):
         "metric": "DiT attention layer ms per chunk with streaming LCSA (random weights), LCSA share",
         "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic: x ~ N(0,1), weights ~ N(0, 1/C), bf16",
+        "dtype": "bf16", "data": "synthetic: x ~ N(0,1), weights ~ N(0, 1/C), bf16", "settle_s": round(settle_s, 2),
         "config": {"workload": f"{w.name} as a DiT layer, cache {args.layer} temporal blocks", "heads": w.heads,
                    "head_dim": w.head_dim, "model_dim": C, "tokens_per_chunk": N, "rope_dims": [44, 42, 42],
                    "selected_pairs": w.batch * w.heads * nnz},
@@ -450,8 +542,10 @@ def cpu_baseline(w, x, sample_blocks):
     flop = kept * 4.0 * 128 * 128 * w.head_dim
     blas = [t for t in threadpool_info() if t.get("user_api") == "blas"]
     cores = max([t.get("num_threads", 1) for t in blas] or [1])
+    vendor = ", ".join(sorted({f"{t.get('internal_api')} {t.get('version')}" for t in blas})) or "unknown"
     return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 2),
+            "seconds": round(dt, 2), "cpu_model": cpu_model(), "blas": vendor,
+            "host_cpus_visible": len(os.sched_getaffinity(0)),
             "sample": f"median of 3 runs; {w.name}: pool+score+select of all {nqb} query blocks, attention of "
                       f"{len(qblocks)} query blocks x {w.batch * w.heads} heads ({kept} kept pairs); "
                       f"numpy fp64, BLAS threads={cores}, elementwise single-threaded"}

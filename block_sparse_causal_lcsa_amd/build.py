@@ -58,5 +58,43 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Build of every source whose host code carries AddressSanitizer and UndefinedBehaviorSanitizer
+# (each -fsanitize= applies to the host pass only, -Xarch_host): the validation, geometry and
+# stream-state code that runs before any launch, checked on the CPU. Device code is built as usual.
+SAN_LIB = os.path.join(OUT, "hostsan", "liblcsa_hostsan.so")
+SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+       "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized() -> str:
+    out = os.path.dirname(SAN_LIB)
+    os.makedirs(out, exist_ok=True)
+    base = [*COMMON, "-Xarch_host", "-g"]
+    jobs = []
+    for src in KERNELS:
+        jobs.append(["hipcc", *base, *DEVICE, *EXTRA.get(src, []), *SAN, "-c",
+                     os.path.join(CSRC, src), "-o", os.path.join(out, src.replace(".hip", ".o"))])
+    for src in HOST:
+        jobs.append(["hipcc", *base, "-ffp-contract=off", *SAN, "-c", os.path.join(CSRC, src), "-o",
+                     os.path.join(out, src.replace(".cpp", ".o"))])
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        list(ex.map(_run, jobs))
+    tmp = SAN_LIB + ".tmp"
+    _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN, "-o", tmp, *[j[-1] for j in jobs]])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (to LD_PRELOAD into a Python that loads
+    the sanitized library)."""
+    r = subprocess.run(["hipcc", "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                       stderr=subprocess.DEVNULL, text=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -16,7 +16,7 @@ extern "C" lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_
   if ((st = check_tensor("q", q, qs, p, hw * p->q_frames)) != LCSA_OK) return st;
   if ((st = check_tensor("k", k, ks, p, hw * p->kv_frames)) != LCSA_OK) return st;
   if ((st = check_tensor("v", v, vs, p, hw * p->kv_frames)) != LCSA_OK) return st;
-  if ((st = check_tensor("o", o, os, p, hw * p->q_frames)) != LCSA_OK) return st;
+  if ((st = check_output_tensor("o", o, os, p, hw * p->q_frames)) != LCSA_OK) return st;
   if (!row_ptr || !col_idx) return fail(LCSA_ERR_INVALID, "lcsa_attn_fwd: row_ptr or col_idx is NULL");
   if (reinterpret_cast<uintptr_t>(row_ptr) % 4 || reinterpret_cast<uintptr_t>(col_idx) % 4 ||
       reinterpret_cast<uintptr_t>(lse) % 4)

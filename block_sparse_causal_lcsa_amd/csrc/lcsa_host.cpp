@@ -115,7 +115,31 @@ lcsa_status check_tensor(const char* name, const void* ptr, lcsa_strides s, cons
                 (long long)s.batch, (long long)s.head, (long long)s.token, p->head_dim);
   if (s.batch % vec || s.head % vec || s.token % vec)
     return fail(LCSA_ERR_INVALID, "%s strides must be multiples of 16 bytes", name);
-  (void)ntok;
+  if (ntok < 1) return fail(LCSA_ERR_INVALID, "%s has no tokens", name);
+  return LCSA_OK;
+}
+
+lcsa_status check_output_tensor(const char* name, void* ptr, lcsa_strides s, const lcsa_problem* p,
+                                int64_t ntok) {
+  lcsa_status st = check_tensor(name, ptr, s, p, ntok);
+  if (st != LCSA_OK) return st;
+  // Every element (b, h, t, c) must have its own address, or two workgroups would write the same
+  // memory. Sort the dimensions of extent > 1 by stride; each stride must step past everything the
+  // smaller dimensions reach.
+  struct Dim { int64_t stride, extent; } d[4] = {
+      {s.batch, p->batch}, {s.head, p->heads}, {s.token, ntok}, {1, p->head_dim}};
+  for (int i = 1; i < 4; ++i)
+    for (int j = i; j > 0 && d[j].stride < d[j - 1].stride; --j) {
+      const Dim t = d[j]; d[j] = d[j - 1]; d[j - 1] = t;
+    }
+  int64_t reach = 0;  // largest offset reached by the dimensions already visited
+  for (int i = 0; i < 4; ++i) {
+    if (d[i].extent <= 1) continue;
+    if (d[i].stride <= reach)
+      return fail(LCSA_ERR_INVALID, "%s strides (%lld, %lld, %lld) make output rows overlap", name,
+                  (long long)s.batch, (long long)s.head, (long long)s.token);
+    reach += (d[i].extent - 1) * d[i].stride;
+  }
   return LCSA_OK;
 }
 

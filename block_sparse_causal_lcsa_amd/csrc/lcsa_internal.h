@@ -26,6 +26,11 @@ int keep_count(const lcsa_problem* p, int n);
 lcsa_status check_tensor(const char* name, const void* ptr, lcsa_strides s, const lcsa_problem* p,
                          int64_t ntok);
 
+// check_tensor, and for a tensor the call writes: no two elements share an address (strides that
+// are zero or that make rows overlap are rejected).
+lcsa_status check_output_tensor(const char* name, void* ptr, lcsa_strides s, const lcsa_problem* p,
+                                int64_t ntok);
+
 // Element size in bytes of the problem's dtype.
 inline int dtype_size(const lcsa_problem* p) { return p->dtype == LCSA_F32 ? 4 : 2; }
 

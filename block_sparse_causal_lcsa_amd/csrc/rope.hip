@@ -125,9 +125,9 @@ extern "C" lcsa_status lcsa_rope_qkv(const lcsa_problem* p, const lcsa_rope* rop
       qkv_token % 8 || qkv_batch % 8 || qkv_batch < 0)
     return fail(LCSA_ERR_INVALID, "lcsa_rope_qkv: qkv NULL, misaligned, or strides that cannot hold a row");
   const int64_t ntok = int64_t(frames) * p->grid_h * p->grid_w;
-  if ((st = check_tensor("q", q, qs, &pc, ntok)) != LCSA_OK) return st;
-  if ((st = check_tensor("k", k, ks, &pc, ntok)) != LCSA_OK) return st;
-  if ((st = check_tensor("v", v, vs, &pc, ntok)) != LCSA_OK) return st;
+  if ((st = check_output_tensor("q", q, qs, &pc, ntok)) != LCSA_OK) return st;
+  if ((st = check_output_tensor("k", k, ks, &pc, ntok)) != LCSA_OK) return st;
+  if ((st = check_output_tensor("v", v, vs, &pc, ntok)) != LCSA_OK) return st;
 
   RopeArgs a{};
   a.qkv = static_cast<const uint16_t*>(qkv);

@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblcsa.so")
+# LCSA_LIBRARY may name another build of the same library (the host-sanitized one that the CPU
+# tests load); by default the in-tree liblcsa.so is loaded.
+LIB_PATH = os.environ.get("LCSA_LIBRARY") or os.path.join(_PKG, "liblcsa.so")
 
 LCSA_OK, LCSA_ERR_INVALID, LCSA_ERR_UNSUPPORTED, LCSA_ERR_HIP = 0, 1, 2, 3
 LCSA_BF16, LCSA_F32 = 0, 1

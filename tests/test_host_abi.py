@@ -152,6 +152,15 @@ def test_bad_pointers_and_strides_rejected_on_host():
     assert lib.lcsa_attn_fwd(ctypes.byref(p), buf, good, buf, good, buf, good, buf, buf, mis, good, None, None) \
         == lcsa.LCSA_ERR_INVALID
     assert b"aligned" in lib.lcsa_last_error()
+    # output views whose rows overlap (two heads or two tokens on the same memory) are rejected:
+    # zero head stride with 12 heads, and a head stride equal to the token stride
+    nq = BASE.nq_tokens
+    for os_ in (lcsa.LcsaStrides(12 * nq * d, 0, d), lcsa.LcsaStrides(12 * nq * d, d, d),
+                lcsa.LcsaStrides(0, nq * d, d)):
+        pp = lcsa.problem(BASE.replace(batch=2)) if os_.batch == 0 else p
+        assert lib.lcsa_attn_fwd(ctypes.byref(pp), buf, good, buf, good, buf, good, buf, buf, buf, os_, None,
+                                 None) == lcsa.LCSA_ERR_INVALID, (os_.batch, os_.head, os_.token)
+        assert b"overlap" in lib.lcsa_last_error()
     big = BASE.replace(kv_frames=40, q_frame0=38)            # 1320 key blocks > one LDS row
     pb = lcsa.problem(big)
     assert lib.lcsa_score_select(ctypes.byref(pb), buf, buf, buf, buf, None, None) == lcsa.LCSA_ERR_UNSUPPORTED
@@ -285,6 +294,11 @@ def test_rope_rejections_on_host():
     assert call(lcsa.LcsaRope(44, 42, 42, 10000.0), frames=3) == lcsa.LCSA_ERR_INVALID
     assert call(lcsa.LcsaRope(44, 42, 42, 10000.0), tok=row - 8) == lcsa.LCSA_ERR_INVALID
     assert call(lcsa.LcsaRope(44, 42, 42, 10000.0), qkv=ctypes.c_void_p((1 << 20) + 4)) == lcsa.LCSA_ERR_INVALID
+    # an output view with every head on the same rows
+    r = lcsa.LcsaRope(44, 42, 42, 10000.0)
+    assert lib.lcsa_rope_qkv(ctypes.byref(p), ctypes.byref(r), buf, 2 * hw * row, row, 0, 2, buf, st, buf,
+                             lcsa.LcsaStrides(12 * 2 * hw * d, 0, d), buf, st, None) == lcsa.LCSA_ERR_INVALID
+    assert b"overlap" in lib.lcsa_last_error()
     pf = lcsa.problem(chunk.replace(dtype="f32"))
     assert call(lcsa.LcsaRope(44, 42, 42, 10000.0), prob=pf) == lcsa.LCSA_ERR_UNSUPPORTED
 

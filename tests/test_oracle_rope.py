@@ -62,3 +62,32 @@ def test_single_pair_closed_form():
     x2[..., 0:2] = [0.0, 1.0]                       # the t pair at frame 3: (0, 1) -> (-sin 3, cos 3)
     y2 = O.rope_3d(p, x2, 3, (2, 2, 2), 10.0)
     np.testing.assert_allclose(y2[0, 0, 1, 0:2], [-np.sin(3), np.cos(3)], atol=1e-15)
+
+
+def test_frequency_schedule_exact_angles():
+    """Every pair of every axis group, not only the first: with theta = 256 and 8 dims per axis the
+    four pairs of a group rotate at 1, 1/4, 1/16 and 1/64 radians per position step (theta raised to
+    minus twice the pair index over the group width), so pair j at position 4^j has turned by exactly
+    one radian and at position 2 * 4^j by two; every other pair of the token is turned by another
+    angle. A schedule with another exponent (pair index over the width, or counting pairs from one)
+    moves these angles and fails here."""
+    theta, dims = 256.0, (8, 8, 8)
+    unit = np.zeros((1, 1, 1, 24))
+    for axis, g0 in (("t", 0), ("h", 8), ("w", 16)):
+        for j in range(4):
+            for turns in (1, 2):
+                pos = turns * 4 ** j
+                x = np.zeros(24)
+                x[g0 + 2 * j] = 1.0                       # (1, 0) in pair j of this axis group
+                if axis == "t":                           # a 1x1 grid at absolute frame pos
+                    p = P.replace(heads=1, head_dim=24, grid_h=1, grid_w=1)
+                    y = O.rope_3d(p, unit + x, pos, dims, theta)[0, 0, 0]
+                elif axis == "h":                         # a column of pos + 1 rows, token at row pos
+                    p = P.replace(heads=1, head_dim=24, grid_h=pos + 1, grid_w=1)
+                    y = O.rope_3d(p, np.broadcast_to(x, (1, 1, pos + 1, 24)).copy(), 0, dims, theta)[0, 0, pos]
+                else:                                     # a row of pos + 1 columns, token at column pos
+                    p = P.replace(heads=1, head_dim=24, grid_h=1, grid_w=pos + 1)
+                    y = O.rope_3d(p, np.broadcast_to(x, (1, 1, pos + 1, 24)).copy(), 0, dims, theta)[0, 0, pos]
+                want = np.zeros(24)
+                want[g0 + 2 * j: g0 + 2 * j + 2] = [np.cos(turns), np.sin(turns)]
+                np.testing.assert_allclose(y, want, atol=1e-12, err_msg=f"axis {axis} pair {j} position {pos}")

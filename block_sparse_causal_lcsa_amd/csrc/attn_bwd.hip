@@ -20,6 +20,7 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <utility>
 
 #include "lcsa_internal.h"
@@ -644,6 +645,43 @@ BwdLayout bwd_layout(const lcsa_problem* p, const Geom& g, int32_t nnz) {
   return l;
 }
 
+// Workspace of lcsa_attn_bwd_noalloc: one static device array per GPU, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (in host code the name is a host-side shadow,
+// not a device address); it uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[LCSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+lcsa_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "lcsa_attn_bwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LCSA_ERR_UNSUPPORTED, "lcsa_attn_bwd_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "lcsa_attn_bwd_noalloc: hipGetSymbolAddress(scratch)");
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256)
+      return fail(LCSA_ERR_HIP, "lcsa_attn_bwd_noalloc: scratch address %p is not 256-byte aligned", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LCSA_OK;
+}
+
+// Both backward entry points: validation, then the four launches. With use_scratch the workspace
+// is this device's static scratch array (workspace and workspace_bytes are ignored).
+lcsa_status attn_bwd_run(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k, lcsa_strides ks,
+                         const void* v, lcsa_strides vs, const void* o, lcsa_strides os, const void* d_o,
+                         lcsa_strides dos, const float* lse, const int32_t* row_ptr, const int32_t* col_idx,
+                         float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream,
+                         bool use_scratch);
+
 }  // namespace
 }  // namespace lcsa
 
@@ -665,6 +703,27 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
                                      const void* d_o, lcsa_strides dos, const float* lse, const int32_t* row_ptr,
                                      const int32_t* col_idx, float* dq, float* dk, float* dv, void* workspace,
                                      size_t workspace_bytes, void* stream) {
+  return attn_bwd_run(p, q, qs, k, ks, v, vs, o, os, d_o, dos, lse, row_ptr, col_idx, dq, dk, dv, workspace,
+                      workspace_bytes, stream, false);
+}
+
+extern "C" lcsa_status lcsa_attn_bwd_noalloc(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
+                                             lcsa_strides ks, const void* v, lcsa_strides vs, const void* o,
+                                             lcsa_strides os, const void* d_o, lcsa_strides dos, const float* lse,
+                                             const int32_t* row_ptr, const int32_t* col_idx, float* dq, float* dk,
+                                             float* dv, void* stream) {
+  return attn_bwd_run(p, q, qs, k, ks, v, vs, o, os, d_o, dos, lse, row_ptr, col_idx, dq, dk, dv, nullptr, 0,
+                      stream, true);
+}
+
+namespace lcsa {
+namespace {
+
+lcsa_status attn_bwd_run(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k, lcsa_strides ks,
+                         const void* v, lcsa_strides vs, const void* o, lcsa_strides os, const void* d_o,
+                         lcsa_strides dos, const float* lse, const int32_t* row_ptr, const int32_t* col_idx,
+                         float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream,
+                         bool use_scratch) {
   Geom g;
   lcsa_status st = validate_problem(p, &g);
   if (st != LCSA_OK) return st;
@@ -675,20 +734,27 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
   if ((st = check_tensor("v", v, vs, p, hw * p->kv_frames)) != LCSA_OK) return st;
   if ((st = check_tensor("o", o, os, p, hw * p->q_frames)) != LCSA_OK) return st;
   if ((st = check_tensor("d_o", d_o, dos, p, hw * p->q_frames)) != LCSA_OK) return st;
-  if (!lse || !row_ptr || !col_idx || !dq || !dk || !dv || !workspace)
+  if (!lse || !row_ptr || !col_idx || !dq || !dk || !dv || (!workspace && !use_scratch))
     return fail(LCSA_ERR_INVALID, "lcsa_attn_bwd: NULL lse, row_ptr, col_idx, gradient or workspace");
   if (reinterpret_cast<uintptr_t>(lse) % 4 || reinterpret_cast<uintptr_t>(row_ptr) % 4 ||
       reinterpret_cast<uintptr_t>(col_idx) % 4 || reinterpret_cast<uintptr_t>(dq) % 16 ||
       reinterpret_cast<uintptr_t>(dk) % 16 || reinterpret_cast<uintptr_t>(dv) % 16 ||
-      reinterpret_cast<uintptr_t>(workspace) % 256)
+      (!use_scratch && reinterpret_cast<uintptr_t>(workspace) % 256))
     return fail(LCSA_ERR_INVALID, "lcsa_attn_bwd: misaligned lse, row_ptr, col_idx, gradient or workspace");
   if ((g.nqb + 31) / 32 > kCscWords)
     return fail(LCSA_ERR_UNSUPPORTED, "lcsa_attn_bwd: more than %d query blocks per head", 32 * kCscWords);
   int32_t nnz = 0;
   if ((st = lcsa_csr_layout(p, nullptr, nullptr, &nnz, nullptr)) != LCSA_OK) return st;
   const BwdLayout l = bwd_layout(p, g, nnz);
-  if (workspace_bytes < l.total)
+  if (use_scratch) {
+    if (l.total > size_t(LCSA_NOALLOC_SCRATCH_BYTES))
+      return fail(LCSA_ERR_UNSUPPORTED,
+                  "lcsa_attn_bwd_noalloc: the problem needs %zu bytes of workspace, more than the %zu-byte "
+                  "static scratch buffer (use lcsa_attn_bwd with a caller workspace)",
+                  l.total, size_t(LCSA_NOALLOC_SCRATCH_BYTES));
+  } else if (workspace_bytes < l.total) {
     return fail(LCSA_ERR_INVALID, "lcsa_attn_bwd: workspace of %zu bytes, %zu needed", workspace_bytes, l.total);
+  }
   const int64_t esz = 2;
   auto span = [&](lcsa_strides s, int64_t ntok) { return (ntok - 1) * s.token * esz + p->head_dim * esz; };
   if (span(qs, hw * p->q_frames) >= (int64_t(1) << 32) || span(ks, hw * p->kv_frames) >= (int64_t(1) << 32) ||
@@ -712,11 +778,6 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  char* w = static_cast<char*>(workspace);
-  a.delta = reinterpret_cast<float*>(w + l.delta);
-  a.lse2 = reinterpret_cast<float*>(w + l.lse2);
-  a.col_ptr = reinterpret_cast<int32_t*>(w + l.col_ptr);
-  a.row_of = reinterpret_cast<int32_t*>(w + l.row_of);
   a.g = g;
   a.heads = p->heads;
   a.nnz = nnz;
@@ -728,6 +789,14 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
   a.k_span = static_cast<uint32_t>(span(ks, hw * p->kv_frames));
   a.v_span = static_cast<uint32_t>(span(vs, hw * p->kv_frames));
   a.do_span = static_cast<uint32_t>(span(dos, hw * p->q_frames));
+  if (use_scratch) {  // every check has passed: only now touch HIP for the scratch address
+    if ((st = scratch_for_current_device(&workspace)) != LCSA_OK) return st;
+  }
+  char* w = static_cast<char*>(workspace);
+  a.delta = reinterpret_cast<float*>(w + l.delta);
+  a.lse2 = reinterpret_cast<float*>(w + l.lse2);
+  a.col_ptr = reinterpret_cast<int32_t*>(w + l.col_ptr);
+  a.row_of = reinterpret_cast<int32_t*>(w + l.row_of);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -767,3 +836,6 @@ extern "C" lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_
   }
   return hip_status(hipGetLastError(), "lcsa_attn_bwd launch");
 }
+
+}  // namespace
+}  // namespace lcsa

@@ -21,7 +21,7 @@ LCSA_OK, LCSA_ERR_INVALID, LCSA_ERR_UNSUPPORTED, LCSA_ERR_HIP = 0, 1, 2, 3
 LCSA_BF16, LCSA_F32 = 0, 1
 
 EXPORTS = ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
-           "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd",
+           "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd", "lcsa_attn_bwd_noalloc",
            "lcsa_stream_state_size", "lcsa_stream_init", "lcsa_stream_reserve", "lcsa_stream_push",
            "lcsa_stream_window", "lcsa_rope_qkv",
            "lcsa_status_string", "lcsa_last_error", "lcsa_version")
@@ -80,6 +80,7 @@ def load():
     lib.lcsa_attn_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.lcsa_attn_bwd.argtypes = [P, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, vp, vp, vp, vp,
                                   ctypes.c_size_t, vp]
+    lib.lcsa_attn_bwd_noalloc.argtypes = [P, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, vp, vp, vp, vp]
     lib.lcsa_rope_qkv.argtypes = [P, ctypes.POINTER(LcsaRope), vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                   ctypes.c_int32, vp, S, vp, S, vp, S, vp]
     SP = ctypes.POINTER(LcsaStream)
@@ -91,7 +92,7 @@ def load():
     lib.lcsa_stream_window.argtypes = [SP, P, ctypes.POINTER(vp), ctypes.POINTER(S), ctypes.POINTER(vp),
                                        ctypes.POINTER(S), ctypes.POINTER(vp)]
     for f in ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
-              "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd", "lcsa_stream_state_size", "lcsa_stream_init",
+              "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd", "lcsa_attn_bwd_noalloc", "lcsa_stream_state_size", "lcsa_stream_init",
               "lcsa_stream_reserve", "lcsa_stream_push", "lcsa_stream_window", "lcsa_rope_qkv"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lcsa_status_string.argtypes = [ctypes.c_int]
@@ -306,6 +307,31 @@ def lcsa_attn_bwd(p: LcsaProblem, q, k, v, o, d_o, lse, row_ptr, col_idx, dq=Non
                                 _ptr(col_idx), _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
     return tuple(grads)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # LCSA_NOALLOC_SCRATCH_BYTES in lcsa.h
+
+
+def lcsa_attn_bwd_noalloc(p: LcsaProblem, q, k, v, o, d_o, lse, row_ptr, col_idx, dq, dk, dv, stream=None):
+    """lcsa_attn_bwd on the library's static per-GPU scratch array: no workspace argument and no
+    allocation anywhere in the call (dq, dk, dv are the caller's)."""
+    hw = p.grid_h * p.grid_w
+    nq, nk = p.q_frames * hw, p.kv_frames * hw
+    for name, t, n in (("q", q, nq), ("k", k, nk), ("v", v, nk), ("o", o, nq), ("d_o", d_o, nq)):
+        _check_token_tensor(name, t, p, n)
+    _check_buffer("lse", lse, _torch().float32, p.batch * p.heads * nq)
+    nqb, _, nnz = _block_counts(p)
+    _check_selection(p, row_ptr, col_idx, nqb, nnz)
+    for name, t, n in (("dq", dq, nq), ("dk", dk, nk), ("dv", dv, nk)):
+        _on_device(name, t)
+        if (t.dtype != _torch().float32 or not t.is_contiguous()
+                or tuple(t.shape) != (p.batch, p.heads, n, p.head_dim)):
+            raise ValueError(f"{name} must be contiguous fp32 [{p.batch}, {p.heads}, {n}, {p.head_dim}]")
+    _check(load().lcsa_attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                                        _strides(v), _ptr(o), _strides(o), _ptr(d_o), _strides(d_o), _ptr(lse),
+                                        _ptr(row_ptr), _ptr(col_idx), _ptr(dq), _ptr(dk), _ptr(dv),
+                                        _stream(stream)))
+    return dq, dk, dv
 
 
 def forward(p: LcsaProblem, q, k, v, row_ptr=None, stream=None):

@@ -152,6 +152,23 @@ lcsa_status lcsa_attn_bwd(const lcsa_problem* p, const void* q, lcsa_strides qs,
                           const int32_t* row_ptr, const int32_t* col_idx, float* dq, float* dk,
                           float* dv, void* workspace, size_t workspace_bytes, void* stream);
 
+/* lcsa_attn_bwd without a caller workspace and without any device allocation, for callers that
+ * cannot allocate: code under HIP graph capture, tight serving or training loops, harnesses that
+ * forbid hipMalloc. Same arguments, arithmetic and results as lcsa_attn_bwd (bit for bit), minus
+ * workspace/workspace_bytes. The workspace is a static device array of LCSA_NOALLOC_SCRATCH_BYTES
+ * per GPU inside the library, held from the first call on that device until the process ends; its
+ * address is looked up once per device (the current device at the call). Problems whose workspace
+ * (lcsa_attn_bwd_workspace_size) exceeds that size return LCSA_ERR_UNSUPPORTED before any launch.
+ * Every call on one GPU shares the array: calls that overlap in time on one GPU (on different
+ * streams, or from different threads) race and give wrong gradients; order them on one stream.
+ * The array needs no initial contents (each call writes what it reads). */
+#define LCSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+lcsa_status lcsa_attn_bwd_noalloc(const lcsa_problem* p, const void* q, lcsa_strides qs, const void* k,
+                                  lcsa_strides ks, const void* v, lcsa_strides vs, const void* o,
+                                  lcsa_strides os, const void* d_o, lcsa_strides dos, const float* lse,
+                                  const int32_t* row_ptr, const int32_t* col_idx, float* dq, float* dk,
+                                  float* dv, void* stream);
+
 /* Streaming state. FlashVSR processes video as a stream of chunks; the attention of a chunk reads
  * the cached K/V of earlier chunks (fmread summary, sec. 2.2 Stage 3: temporal consistency is
  * refined through the KV cache of later layers; sec. 3, efficiency analysis: streaming adds only an

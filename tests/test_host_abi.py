@@ -197,6 +197,27 @@ def test_backward_rejections_on_host():
     assert b"bf16" in lib.lcsa_last_error()
 
 
+def test_noalloc_backward_rejects_a_problem_beyond_its_scratch_on_host():
+    # a 26-frame clip at 1536x2688 needs more workspace than the static scratch array holds: rejected
+    # during validation, before any HIP call
+    lib = lcsa.load()
+    big = W.UHD_TRUNC.replace(kv_frames=26, q_frame0=0, q_frames=26)
+    p = lcsa.problem(big)
+    n = ctypes.c_size_t(0)
+    assert lib.lcsa_attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == lcsa.LCSA_OK
+    assert n.value > lcsa.NOALLOC_SCRATCH_BYTES
+    buf = ctypes.c_void_p(1 << 20)   # never dereferenced
+    st = lcsa.LcsaStrides(big.heads * big.nq_tokens * big.head_dim, big.nq_tokens * big.head_dim, big.head_dim)
+    r = lib.lcsa_attn_bwd_noalloc(ctypes.byref(p), buf, st, buf, st, buf, st, buf, st, buf, st, buf, buf, buf,
+                                  buf, buf, buf, None)
+    assert r == lcsa.LCSA_ERR_UNSUPPORTED
+    assert b"static scratch" in lib.lcsa_last_error()
+    # and a NULL gradient is still rejected as invalid
+    r = lib.lcsa_attn_bwd_noalloc(ctypes.byref(p), buf, st, buf, st, buf, st, buf, st, buf, st, buf, buf, buf,
+                                  None, buf, buf, None)
+    assert r == lcsa.LCSA_ERR_INVALID
+
+
 def test_stream_struct_layout_matches_header(tmp_path):
     src = tmp_path / "slayout.c"
     fields = [f[0] for f in lcsa.LcsaStream._fields_]

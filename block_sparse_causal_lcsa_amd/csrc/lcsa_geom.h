@@ -107,9 +107,18 @@ LCSA_HD int block_cols(const Geom& g, int wb) {
 // returns the last visible temporal block. With a token-granular window a key block is visible when
 // some token of i sees some token of it: per axis, the union of the windows of i's tokens, which is
 // [lo(first), hi(last)] since the bounds are monotone.
+LCSA_HD void qblock_window_at(const Geom& g, int hb, int wb, int* h0, int* h1, int* w0, int* w1);
+
 LCSA_HD int qblock_window(const Geom& g, int i, int* h0, int* h1, int* w0, int* w1) {
   int tb, hb, wb;
   qblock_coords(g, i, &tb, &hb, &wb);
+  qblock_window_at(g, hb, wb, h0, h1, w0, w1);
+  return tb;
+}
+
+// The window of query block (hb, wb) (any temporal block): inclusive key-block rows [h0, h1] and
+// columns [w0, w1].
+LCSA_HD void qblock_window_at(const Geom& g, int hb, int wb, int* h0, int* h1, int* w0, int* w1) {
   if (token_window(g)) {
     const bool pres = g.win_mode == kWinTokenPreserving;
     int lo, hi, lo2, hi2;
@@ -121,11 +130,10 @@ LCSA_HD int qblock_window(const Geom& g, int i, int* h0, int* h1, int* w0, int* 
     tok_range(pres, 8 * wb + block_cols(g, wb) - 1, g.W, g.wtw, &lo2, &hi2);
     *w0 = lo / 8;
     *w1 = hi2 / 8;
-    return tb;
+    return;
   }
   win_range(g.win_mode, hb, g.Hb, g.wbh, h0, h1);
   win_range(g.win_mode, wb, g.Wb, g.wbw, w0, w1);
-  return tb;
 }
 
 // Unsigned division by a run-time constant d >= 1 as one multiply and a shift (Granlund-Montgomery

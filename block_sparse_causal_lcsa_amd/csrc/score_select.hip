@@ -2,16 +2,24 @@
 // (FlashVSR summary, sec. 2.2: a coarse block-to-block attention map from the pooled features,
 // the Top-K most relevant block pairs are kept; sec. 2.3: the local spatial window).
 //
-// One workgroup (16 or 4 waves) per (batch, head, tile of 16 or 4 query blocks).
-//  1. Scores: s_ij = scale * <qbar_i, kbar_j> for the tile's 16 rows against every key block up to
-//     the last temporal block the tile can see, as fp64 MFMA 16x16x4 tiles (the pooled fp32
-//     features are widened exactly). Column tiles with no visible entry are skipped. Rows of 16
-//     fp64 scores live in LDS, -inf where the key block is not visible.
-//  2. Selection, one wave per row (all 16 rows in parallel): scores map to order-preserving 64-bit keys; a most-significant-
-//     bit-first radix select over the wave's candidates (ballot + popcount per bit) finds the key of
-//     the K_i-th largest score and how many of the keys equal to it are still needed; equal keys are
-//     taken lowest index first. Kept indices are emitted in ascending order with ballot prefix sums.
+// One workgroup per (batch, head, tile of kRows consecutive query blocks), one wave per query block.
+//  1. Candidates. The tile's candidate set is the union of its rows' visible sets: the temporal
+//     blocks up to the last one any row sees, times the smallest rectangle of block rows and columns
+//     holding every row's window. It is enumerated in ascending key-block index (temporal block, then
+//     block row, then block column), so no row holds more than its tile's union, whatever the number
+//     of key blocks; a row's own mask is applied to the union when the scores are stored.
+//  2. Scores: s_ij = scale * <qbar_i, kbar_j> in fp64 (the fp32 pooled features widen exactly), with
+//     v_mfma_f64_4x4x4 in its 4-block form: one instruction scores the tile's 4 rows against 16
+//     candidates over 4 channels. Scores sit in LDS, [row][candidate], -inf where not visible.
+//  3. Selection, one wave per row: scores map to order-preserving 64-bit keys held in registers; a
+//     bisection over the key range, counting the keys at or above the midpoint with one ballot and
+//     popcount per register, finds the key T of the K_i-th largest score (it stops early when some
+//     threshold leaves exactly K_i keys at or above it). Keys above T are kept, keys equal to T lowest
+//     index first; kept indices are emitted ascending with ballot prefix sums.
 // The selection is exact for the fp64 scores: the largest K_i scores, exact ties to the lower j.
+// Workgroups are ordered so that each XCD (hardware deals workgroup n to XCD n mod 8) takes one
+// contiguous run of the (batch, head)-major tiles: a head's tiles share one or two XCDs' L2, which
+// then serves its pooled K to all of them, and every XCD gets the same number of tiles.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -23,14 +31,8 @@
 namespace lcsa {
 namespace {
 
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-
-// ROWS query blocks per workgroup, one wave each: 16 shares each loaded pooled-K tile among 16
-// rows; 4 gives four times the workgroups when a problem has too few rows to fill the chip.
-constexpr int kRowsWide = 16, kRowsNarrow = 4;
-constexpr int kMaxCols = 1248;            // key blocks one row can hold in LDS
-constexpr int kMaxSlots = (kMaxCols + 63) / 64;
-constexpr int kLdsPad = 2;
+constexpr int kXcds = 8;
+constexpr int kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
 
 struct SelArgs {
   const float* qp;     // [B*Hh, nqb, D]
@@ -40,26 +42,35 @@ struct SelArgs {
   double* dbg;         // [B*Hh, nqb, nkb] or null
   Geom g;
   int32_t nnz;
-  int32_t ld;          // LDS row stride in doubles
+  int32_t bh;          // batch * heads
+  int32_t tiles;       // query-block tiles per (batch, head)
+  int32_t nwg;         // bh * tiles workgroups
+  int32_t ld;          // LDS row stride of the scores, in doubles
   double scale;
+  FastDiv div_bpt, div_wb;  // division by g.bpt and g.Wb
 };
 
-__device__ __forceinline__ bool is_visible(const Geom& g, int tbi, int h0, int h1, int w0, int w1, int j) {
-  const int tbj = j / g.bpt, rem = j - (j / g.bpt) * g.bpt;
-  const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
-  return tbj <= tbi && hb >= h0 && hb <= h1 && wb >= w0 && wb <= w1;
-}
+// A tile's candidate set: temporal blocks [0, nt), block rows [h0, h0 + nh), columns [w0, w0 + nw).
+struct Union {
+  int nt, h0, nh, w0, nw;
+  LCSA_HD int size() const { return nt * nh * nw; }
+};
 
-// Inclusive prefix sum over the 64 lanes of a wave (lane order), with DPP row shifts inside each
-// 16-lane row and row broadcasts across rows.
-__device__ __forceinline__ int wave_inclusive_sum(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15 into rows 1 and 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31 into rows 2 and 3
-  return v;
+LCSA_HD Union tile_union(const Geom& g, int r0, int rows) {
+  Union u{0, 1 << 30, 0, 1 << 30, 0};
+  int h1 = -1, w1 = -1;
+  for (int r = 0; r < rows; ++r) {
+    int a0, a1, b0, b1;
+    const int tb = qblock_window(g, r0 + r, &a0, &a1, &b0, &b1);
+    u.nt = tb + 1 > u.nt ? tb + 1 : u.nt;
+    u.h0 = a0 < u.h0 ? a0 : u.h0;
+    u.w0 = b0 < u.w0 ? b0 : u.w0;
+    h1 = a1 > h1 ? a1 : h1;
+    w1 = b1 > w1 ? b1 : w1;
+  }
+  u.nh = h1 - u.h0 + 1;
+  u.nw = w1 - u.w0 + 1;
+  return u;
 }
 
 __device__ __forceinline__ uint64_t order_key(double s) {
@@ -67,187 +78,313 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-template <int D, int SLOTS, int kRows>
-__global__ __launch_bounds__(64 * kRows) void score_select_kernel(SelArgs a) {
-  extern __shared__ double S[];  // [kRows][a.ld]
-  const Geom& g = a.g;
-  const int tiles = (g.nqb + kRows - 1) / kRows;
-  const int bh = blockIdx.x / tiles;
-  const int r0 = (blockIdx.x - bh * tiles) * kRows;
-  const int rows = min(kRows, g.nqb - r0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
+// floor(u / d) for 0 <= u < 2^22 and 1 <= d, with rcp = 1.0f / d: the float product is within 1/2 of
+// the quotient, so one correction either way makes it exact.
+__device__ __forceinline__ int udiv_small(int u, int d, float rcp) {
+  int q = int(float(u) * rcp);
+  q -= q * d > u;
+  q += (q + 1) * d <= u;
+  return q;
+}
 
-  // key blocks up to the last temporal block visible from the tile's last row
-  const int tb_last = g.q_tb0 + (r0 + rows - 1) / g.bpt;
-  const int ncol = min((tb_last + 1) * g.bpt, g.nkb);
-  const int nct = (ncol + 15) / 16;
+// Position of candidate u in a tile's union: temporal block t, block row hb, block column wb.
+struct UnionDiv {
+  int hw;
+  float rcp_hw, rcp_nw;
+};
 
-  const float* qrow = a.qp + (int64_t(bh) * g.nqb + r0 + min(lr, rows - 1)) * D;
-  const float* kmat = a.kp + int64_t(bh) * g.nkb * D;
+__device__ __forceinline__ void union_pos(const Union& un, const UnionDiv& ud, int u, int* t, int* hb, int* wb) {
+  *t = udiv_small(u, ud.hw, ud.rcp_hw);
+  const int rem = u - *t * ud.hw;
+  const int dh = udiv_small(rem, un.nw, ud.rcp_nw);
+  *hb = un.h0 + dh;
+  *wb = un.w0 + rem - dh * un.nw;
+}
 
-  // A operand (16 query rows x 4 channels per step). Lane (lr, lg) supplies row lr; k-step
-  // 4m+e covers channels 16m + 4*lg + e, so each lane reads float4s; B uses the same mapping.
-  float4 qa[D / 16];
+// Key block of candidate u of a tile's union.
+__device__ __forceinline__ int union_block(const Geom& g, const Union& un, const UnionDiv& ud, int u) {
+  int t, hb, wb;
+  union_pos(un, ud, u, &t, &hb, &wb);
+  return (t * g.Hb + hb) * g.Wb + wb;
+}
+
+// Keys of a row's candidates u = lane + 64 m (m < SLOTS) as high and low 32-bit halves; 0 for masked
+// entries and u >= U, below every candidate key (a candidate's high half is at least 2^20). SLOTS = 0:
+// the row is longer than the registers hold and every pass reads the scores from LDS again.
+template <int SLOTS>
+struct RowKeys {
+  uint32_t hi[SLOTS > 0 ? SLOTS : 1], lo[SLOTS > 0 ? SLOTS : 1];
+};
+
+// Count of this wave's candidates whose key has high half >= th (PHASE 0), or high half == th and low
+// half >= tl (PHASE 1). th >= 1, so masked entries never count.
+template <int SLOTS, int PHASE>
+__device__ __forceinline__ int count_keys(const RowKeys<SLOTS>& rk, const double* srow, int U, int lane, uint32_t th,
+                                          uint32_t tl) {
+  int c = 0;
+  if constexpr (SLOTS > 0) {
 #pragma unroll
-  for (int m = 0; m < D / 16; ++m) qa[m] = *reinterpret_cast<const float4*>(qrow + 16 * m + 4 * lg);
-
-  // window of the 4 output rows this lane holds in the MFMA result (rows lg + 4*rr)
-  int tbi[4], h0[4], h1[4], w0[4], w1[4];
-  bool rv[4];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int i = r0 + lg + 4 * rr;
-    rv[rr] = i < g.nqb && (lg + 4 * rr) < rows;
-    tbi[rr] = qblock_window(g, rv[rr] ? i : r0, &h0[rr], &h1[rr], &w0[rr], &w1[rr]);
+    for (int m = 0; m < SLOTS; ++m)
+      c += __popcll(__ballot(PHASE == 0 ? rk.hi[m] >= th : (rk.hi[m] == th && rk.lo[m] >= tl)));
+  } else {
+    for (int u0 = 0; u0 < U; u0 += 64) {
+      const double x = u0 + lane < U ? srow[u0 + lane] : -INFINITY;
+      const uint64_t k = x != -INFINITY ? order_key(x) : 0;
+      const uint32_t h = uint32_t(k >> 32), l = uint32_t(k);
+      c += __popcll(__ballot(PHASE == 0 ? h >= th : (h == th && l >= tl)));
+    }
   }
+  return c;
+}
 
-  for (int ct = wave; ct < nct; ct += kRows) {
-    const int j = ct * 16 + lr;
-    bool vis[4];
-    bool any = false;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      vis[rr] = rv[rr] && j < ncol && is_visible(g, tbi[rr], h0[rr], h1[rr], w0[rr], w1[rr], j);
-      any |= vis[rr];
+// Largest t in [lo, hi] with count(t) >= need, given count(lo) >= need (count non-increasing in t);
+// stops early at a t whose count is exactly `need` (then *exact is set). Uniform scalar loop.
+template <typename F>
+__device__ __forceinline__ uint32_t bisect(uint32_t lo, uint32_t hi, int need, bool* exact, F&& count) {
+  *exact = false;
+  while (lo < hi) {
+    const uint32_t mid = lo + (hi - lo) / 2 + 1;
+    const int c = count(mid);
+    if (c == need) {
+      *exact = true;
+      return mid;
     }
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-    if (__any(any)) {
-      const float* krow = kmat + int64_t(min(j, ncol - 1)) * D;
-      // four independent accumulation chains (channel e of each float4), summed in a fixed order
-      f64x4 c[4] = {acc, acc, acc, acc};
+    if (c > need) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int D, int kRows, int SLOTS>
+__global__ __launch_bounds__(64 * kRows) void score_select_kernel(SelArgs a) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  extern __shared__ double S[];  // [kRows][a.ld] scores
+  const Geom& g = a.g;
+  // XCD-contiguous order over the (batch, head)-major tiles
+  int wg = blockIdx.x;
+  const int n8 = (a.nwg / kXcds) * kXcds;
+  if (wg < n8) wg = (wg % kXcds) * (a.nwg / kXcds) + wg / kXcds;
+  const int bh = wg / a.tiles;
+  const int r0 = (wg - bh * a.tiles) * kRows;
+  const int rows = min(kRows, g.nqb - r0);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // this wave's row of the selection: its CSR range, loaded early (uniform scalar loads)
+  const int i_sel = r0 + (wave < rows ? wave : 0);
+  const int rp_beg = __builtin_amdgcn_readfirstlane(a.row_ptr[i_sel]);
+  const int K = __builtin_amdgcn_readfirstlane(a.row_ptr[i_sel + 1]) - rp_beg;
+
+  // ---- scores. v_mfma_f64_4x4x4f64, 4 blocks: block b (0..3) multiplies A_b (4 rows x 4 k) by
+  // B_b (4 k x 4 columns). A_b[i][k] comes from lane 16k + 4b + i, B_b[k][j] from lane 16k + 4b + j,
+  // and D_b[i][j] lands in lane 16i + 4b + j. Every block takes the tile's 4 rows as A, block b takes
+  // candidates 4b..4b+3 of the column tile as B: one instruction = 4 rows x 16 candidates x 4 channels.
+  // Channel order within the dot product: step s (0..D/4-1) and k give channel (D/4) k + s, so each lane
+  // reads one contiguous run of D/4 channels of its row and of its candidate.
+  constexpr int KR = D / 4;  // channels per lane
+  const int lk = lane >> 4;
+  const int qi = lane & 3;   // A row of this lane
+  const int lc = lane & 15;  // B column (candidate within the column tile) of this lane
+  float4 qf[KR / 4];
+  {
+    const int qrow = r0 + (qi < rows ? qi : 0);
+    const float4* src = reinterpret_cast<const float4*>(a.qp + (int64_t(bh) * g.nqb + qrow) * D + KR * lk);
 #pragma unroll
-      for (int m = 0; m < D / 16; ++m) {
-        const float4 kb = *reinterpret_cast<const float4*>(krow + 16 * m + 4 * lg);
-        c[0] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].x, (double)kb.x, c[0], 0, 0, 0);
-        c[1] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].y, (double)kb.y, c[1], 0, 0, 0);
-        c[2] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].z, (double)kb.z, c[2], 0, 0, 0);
-        c[3] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[m].w, (double)kb.w, c[3], 0, 0, 0);
+    for (int v = 0; v < KR / 4; ++v) qf[v] = src[v];
+  }
+  // each row's own window (candidate test when the scores are stored) and the tile's union
+  int tbi[kRows], h0[kRows], h1[kRows], w0[kRows], w1[kRows];
+  Union un{0, 1 << 30, 0, 1 << 30, 0};
+  {
+    int uh1 = -1, uw1 = -1;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const uint32_t ir = uint32_t(r0 + (r < rows ? r : 0));
+      const uint32_t tr = fast_div(ir, a.div_bpt), rem = ir - tr * uint32_t(g.bpt);
+      const uint32_t hb = fast_div(rem, a.div_wb), wb = rem - hb * uint32_t(g.Wb);
+      tbi[r] = g.q_tb0 + int(tr);
+      qblock_window_at(g, int(hb), int(wb), &h0[r], &h1[r], &w0[r], &w1[r]);
+      un.nt = max(un.nt, tbi[r] + 1);
+      un.h0 = min(un.h0, h0[r]);
+      un.w0 = min(un.w0, w0[r]);
+      uh1 = max(uh1, h1[r]);
+      uw1 = max(uw1, w1[r]);
+    }
+    un.nh = uh1 - un.h0 + 1;
+    un.nw = uw1 - un.w0 + 1;
+  }
+  const UnionDiv ud{un.nh * un.nw, 1.0f / float(un.nh * un.nw), 1.0f / float(un.nw)};
+  const int U = un.size();
+  const int nct = (U + 15) / 16;  // 16-candidate column tiles
+  const float* kmat = a.kp + int64_t(bh) * g.nkb * D;
+  auto load_col = [&](int ct, float4 (&kb)[KR / 4]) __attribute__((always_inline)) {
+    const int u = min(16 * ct + lc, U - 1);
+    const float4* src = reinterpret_cast<const float4*>(kmat + int64_t(union_block(g, un, ud, u)) * D + KR * lk);
+#pragma unroll
+    for (int v = 0; v < KR / 4; ++v) kb[v] = src[v];
+  };
+  // this wave's column tiles ct = wave + kRows n; the loads of PF of them are in flight at a time
+  constexpr int PF = 4;
+  float4 kb[PF][KR / 4];
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (wave + kRows * p < nct) load_col(wave + kRows * p, kb[p]);
+  double qa[KR];
+#pragma unroll
+  for (int v = 0; v < KR / 4; ++v) {
+    qa[4 * v] = qf[v].x; qa[4 * v + 1] = qf[v].y; qa[4 * v + 2] = qf[v].z; qa[4 * v + 3] = qf[v].w;
+  }
+  const int orow = lane >> 4;  // result row of this lane
+  for (int n = 0; wave + kRows * n < nct; n += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int ct = wave + kRows * (n + p);
+      if (ct >= nct) break;
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};  // four independent chains, summed in a fixed order
+#pragma unroll
+      for (int v = 0; v < KR / 4; ++v) {
+        acc[0] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v], (double)kb[p][v].x, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 1], (double)kb[p][v].y, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 2], (double)kb[p][v].z, acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 3], (double)kb[p][v].w, acc[3], 0, 0, 0);
       }
-      acc = (c[0] + c[1]) + (c[2] + c[3]);
-    }
-    // result item rr of lane (lr, lg) is D[row lg + 4*rr][col lr]
+      if (ct + kRows * PF < nct) load_col(ct + kRows * PF, kb[p]);
+      const double sc = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * a.scale;
+      const int u = 16 * ct + lc;
+      if (u < U && orow < kRows) {
+        int t, hb, wb;
+        union_pos(un, ud, u, &t, &hb, &wb);
+        bool vis = false;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      if (lg + 4 * rr < kRows) S[(lg + 4 * rr) * a.ld + j] = vis[rr] ? acc[rr] * a.scale : -INFINITY;
+        for (int r = 0; r < kRows; ++r)
+          if (r == orow) vis = r < rows && t <= tbi[r] && hb >= h0[r] && hb <= h1[r] && wb >= w0[r] && wb <= w1[r];
+        S[orow * a.ld + u] = vis ? sc : -INFINITY;
+      }
+    }
   }
   __syncthreads();
 
-  const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
-  for (int rl = wave; rl < rows; rl += kRows) {
-    const int i = r0 + rl;
-    const double* srow = S + rl * a.ld;
-    if (a.dbg) {
-      double* drow = a.dbg + (int64_t(bh) * g.nqb + i) * g.nkb;
-      for (int j = lane; j < g.nkb; j += 64) drow[j] = j < ncol ? srow[j] : -INFINITY;
+  // ---- selection: wave rl selects row r0 + rl
+  const int rl = wave;
+  if (rl >= rows) return;
+  const int i = r0 + rl;
+  const double* srow = S + rl * a.ld;
+  if (a.dbg) {
+    double* drow = a.dbg + (int64_t(bh) * g.nqb + i) * g.nkb;
+    const int hw = un.nh * un.nw;
+    for (int j = lane; j < g.nkb; j += 64) {
+      const int t = j / g.bpt, rem = j - t * g.bpt;
+      const int hb = rem / g.Wb, wb = rem - (rem / g.Wb) * g.Wb;
+      const bool in = t < un.nt && hb >= un.h0 && hb < un.h0 + un.nh && wb >= un.w0 && wb < un.w0 + un.nw;
+      drow[j] = in ? srow[t * hw + (hb - un.h0) * un.nw + (wb - un.w0)] : -INFINITY;
     }
-    const int K = a.row_ptr[i + 1] - a.row_ptr[i];
-    int32_t* out = a.col_idx + int64_t(bh) * a.nnz + a.row_ptr[i];
-
-    // non-candidates (masked, beyond the row) get key 0, below every candidate's key; the loops
-    // below are branch-free over a fixed slot count
-    uint64_t key[SLOTS];
-    int ncand = 0;
-#pragma unroll
-    for (int m = 0; m < SLOTS; ++m) {
-      const int j = lane + 64 * m;
-      const double s = j < ncol ? srow[j] : -INFINITY;
-      const bool c = s != -INFINITY;
-      key[m] = c ? order_key(s) : 0;
-      ncand += __popcll(__ballot(c));
-    }
-    int need = min(K, ncand);
-    uint64_t prefix = 0, mask = 0;
-    int eq = ncand;  // candidates whose masked key equals the prefix
-    // Most-significant-digit-first radix select, 8-bit digits: per digit, a histogram (this wave's
-    // score row, no longer needed, serves as 256 counters) of the candidates that match the prefix,
-    // a suffix scan from the largest digit and the digit where the K_i-th largest key lies.
-    uint32_t* hist = reinterpret_cast<uint32_t*>(S + rl * a.ld);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) hist[4 * lane + k] = 0;
-    for (int shift = 56; shift >= 0 && eq != need; shift -= 8) {
-#pragma unroll
-      for (int m = 0; m < SLOTS; ++m)
-        if (key[m] != 0 && (key[m] & mask) == prefix) atomicAdd(&hist[(key[m] >> shift) & 255], 1u);
-      // lane L holds digits 255 - 4L - k, k = 0..3 (descending)
-      uint32_t c[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = hist[255 - 4 * lane - k];
-      const int tot = int(c[0] + c[1] + c[2] + c[3]);
-      const int incl = wave_inclusive_sum(tot);  // candidates with digit >= 252 - 4L
-      const uint64_t reach = __ballot(incl >= need);
-      const int L = __builtin_ctzll(reach);       // first lane whose range holds the need-th key
-      int above = __shfl(incl - tot, L);          // candidates with a larger digit than lane L's
-      int d = 255 - 4 * L, cnt = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int ck = __shfl(int(c[k]), L);
-        if (cnt == 0 && above + ck >= need) {
-          d = 255 - 4 * L - k;
-          cnt = ck;
-        } else if (cnt == 0) {
-          above += ck;
-        }
-      }
-      need -= above;
-      eq = cnt;
-      prefix |= uint64_t(d) << shift;
-      mask |= uint64_t(255) << shift;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) hist[4 * lane + k] = 0;
-    }
-    // kept: masked key above the prefix, or equal to it and among the first `need` such (by j);
-    // key 0 is never kept (a kept key is at least the K-th largest candidate key, which is > 0)
-    int written = 0, ties = 0;
-#pragma unroll
-    for (int m = 0; m < SLOTS; ++m) {
-      const uint64_t km = key[m] & mask;
-      const bool c = key[m] != 0;
-      const bool tie = c & (km == prefix);
-      const uint64_t tb = __ballot(tie);
-      const bool sel = (c & (km > prefix)) | (tie & (ties + __popcll(tb & lt_mask) < need));
-      ties += __popcll(tb);
-      const uint64_t sb = __ballot(sel);
-      if (sel) out[written + __popcll(sb & lt_mask)] = lane + 64 * m;
-      written += __popcll(sb);
-    }
-    for (int s = written + lane; s < K; s += 64) out[s] = -1;  // only if row_ptr asks for > n_i
   }
+  int32_t* out = a.col_idx + int64_t(bh) * a.nnz + rp_beg;
+  RowKeys<SLOTS> rk;
+  int ncand = 0;
+  if constexpr (SLOTS > 0) {
+#pragma unroll
+    for (int m = 0; m < SLOTS; ++m) {
+      const int u = lane + 64 * m;
+      const double x = u < U ? srow[u] : -INFINITY;
+      const uint64_t k = x != -INFINITY ? order_key(x) : 0;
+      rk.hi[m] = uint32_t(k >> 32);
+      rk.lo[m] = uint32_t(k);
+      ncand += __popcll(__ballot(k != 0));
+    }
+  } else {
+    ncand = count_keys<SLOTS, 0>(rk, srow, U, lane, 1, 0);
+  }
+  // The kept set: keys above the threshold (th, tl), plus the first `ties` keys equal to it (by
+  // index); ties == 0 means every key >= (th, tl) and no other. First the high halves are bisected;
+  // only when the K_i-th key shares its high half with a key that is not kept (scores within about
+  // 2^-20 relative of each other) are the low halves bisected among that high half.
+  const int need = min(K, ncand);
+  uint32_t th = 1, tl = 0;
+  int ties = 0;
+  if (need < ncand) {
+    bool exact;
+    th = bisect(1u, ~0u, need, &exact,
+                [&](uint32_t t) { return count_keys<SLOTS, 0>(rk, srow, U, lane, t, 0); });
+    if (!exact) {
+      const int above = th == ~0u ? 0 : count_keys<SLOTS, 0>(rk, srow, U, lane, th + 1, 0);
+      const int need2 = need - above;  // >= 1 of the keys with high half th
+      tl = bisect(0u, ~0u, need2, &exact,
+                  [&](uint32_t t) { return count_keys<SLOTS, 1>(rk, srow, U, lane, th, t); });
+      if (!exact) {
+        const int above2 = tl == ~0u ? 0 : count_keys<SLOTS, 1>(rk, srow, U, lane, th, tl + 1);
+        ties = need2 - above2;
+      }
+    }
+  }
+  // emit ascending
+  const uint64_t T = (uint64_t(th) << 32) | tl;
+  const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
+  int written = 0, seen = 0;
+  auto emit = [&](int u, uint64_t k) __attribute__((always_inline)) {
+    const bool c = k != 0;
+    const bool tie = c & (ties > 0) & (k == T);
+    const uint64_t tb = __ballot(tie);
+    const bool sel = c & (ties > 0 ? (k > T || (tie && seen + __popcll(tb & lt_mask) < ties)) : (k >= T));
+    seen += __popcll(tb);
+    const uint64_t sb = __ballot(sel);
+    if (sel) out[written + __popcll(sb & lt_mask)] = union_block(g, un, ud, u);
+    written += __popcll(sb);
+  };
+  if constexpr (SLOTS > 0) {
+#pragma unroll
+    for (int m = 0; m < SLOTS; ++m) {
+      if (64 * m >= U) break;
+      emit(lane + 64 * m, (uint64_t(rk.hi[m]) << 32) | rk.lo[m]);
+    }
+  } else {
+    for (int u0 = 0; u0 < U; u0 += 64) {
+      const double x = u0 + lane < U ? srow[u0 + lane] : -INFINITY;
+      emit(u0 + lane, x != -INFINITY ? order_key(x) : 0);
+    }
+  }
+  for (int s = written + lane; s < K; s += 64) out[s] = -1;  // only if row_ptr asks for > n_i
 }
 
-// The dynamic-LDS limit of each kernel instantiation is raised once per device (to the largest
-// size a row can need), not on every call, so that launches can be captured into a HIP graph.
+// The dynamic-LDS limit of each kernel instantiation is raised once per device (to the whole LDS),
+// not on every call, so that launches can be captured into a HIP graph.
 constexpr int kMaxDevices = 64;
 
-template <int D, int SLOTS, int kRows>
-lcsa_status launch(const SelArgs& a, const Geom& g, int bh, hipStream_t s) {
+template <int D, int kRows, int SLOTS>
+lcsa_status launch(SelArgs a, int max_union, hipStream_t s) {
   static std::atomic<uint64_t> raised[kMaxDevices];
   int dev = 0;
   lcsa_status st = hip_status(hipGetDevice(&dev), "lcsa_score_select device");
   if (st != LCSA_OK) return st;
   if (dev < 0 || dev >= kMaxDevices) return fail(LCSA_ERR_UNSUPPORTED, "lcsa_score_select: device %d", dev);
   if (raised[dev].load(std::memory_order_acquire) == 0) {
-    const size_t max_lds = size_t(kRows) * (((kMaxCols + 15) / 16) * 16 + kLdsPad) * sizeof(double);
-    st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<D, SLOTS, kRows>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(max_lds)),
+    st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<D, kRows, SLOTS>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes),
                     "lcsa_score_select LDS size");
     if (st != LCSA_OK) return st;
     raised[dev].store(1, std::memory_order_release);
   }
+  a.ld = ((max_union + 15) / 16) * 16 + 2;  // the pad spreads the 4 rows of a store over the banks
   const size_t lds = size_t(kRows) * a.ld * sizeof(double);
-  const int wgs = bh * ((g.nqb + kRows - 1) / kRows);
-  score_select_kernel<D, SLOTS, kRows><<<wgs, 64 * kRows, lds, s>>>(a);
+  a.tiles = (a.g.nqb + kRows - 1) / kRows;
+  a.nwg = a.bh * a.tiles;
+  score_select_kernel<D, kRows, SLOTS><<<a.nwg, 64 * kRows, lds, s>>>(a);
   return LCSA_OK;
 }
 
-// Rows per workgroup: 16 unless that leaves fewer than 128 workgroups (half the CUs), then 4
-// (measured at the 768x1408 chunk, 60 -> 204 workgroups: 21 -> 14 us; at the 1536x2688 chunk,
-// with 192 workgroups of 16, the narrow form was slower: it reloads pooled K per 4 rows).
-template <int D, int SLOTS>
-lcsa_status launch_rows(const SelArgs& a, const Geom& g, int bh, hipStream_t s) {
-  if (bh * ((g.nqb + kRowsWide - 1) / kRowsWide) >= 128) return launch<D, SLOTS, kRowsWide>(a, g, bh, s);
-  return launch<D, SLOTS, kRowsNarrow>(a, g, bh, s);
+// Register slots of 64 candidates for the longest row: 4, 8, 16 or 32; beyond 2048 candidates the
+// selection reads the scores from LDS on every pass (0).
+template <int D, int kRows>
+lcsa_status launch_slots(const SelArgs& a, int max_union, hipStream_t s) {
+  const int slots = (max_union + 63) / 64;
+  if (slots <= 4) return launch<D, kRows, 4>(a, max_union, s);
+  if (slots <= 8) return launch<D, kRows, 8>(a, max_union, s);
+  if (slots <= 16) return launch<D, kRows, 16>(a, max_union, s);
+  if (slots <= 32) return launch<D, kRows, 32>(a, max_union, s);
+  return launch<D, kRows, 0>(a, max_union, s);
 }
+
+// LDS bytes a workgroup of `rows` rows needs for a union of `u` candidates.
+size_t lds_need(int rows, int u) { return size_t(rows) * (((u + 15) / 16) * 16 + 2) * sizeof(double); }
 
 }  // namespace
 }  // namespace lcsa
@@ -266,29 +403,40 @@ extern "C" lcsa_status lcsa_score_select(const lcsa_problem* p, const float* q_p
       reinterpret_cast<uintptr_t>(row_ptr) % 4 || reinterpret_cast<uintptr_t>(col_idx) % 4 ||
       reinterpret_cast<uintptr_t>(scores_dbg) % 8)
     return fail(LCSA_ERR_INVALID, "lcsa_score_select: misaligned pointer");
-  if (g.nkb > kMaxCols)
-    return fail(LCSA_ERR_UNSUPPORTED, "lcsa_score_select: %d key blocks exceed the %d a row can hold",
-                g.nkb, kMaxCols);
   int32_t nnz = 0;
   if ((st = lcsa_csr_layout(p, nullptr, nullptr, &nnz, nullptr)) != LCSA_OK) return st;
-  SelArgs a{q_pooled, k_pooled, row_ptr, col_idx, scores_dbg, g, nnz, 0, static_cast<double>(p->scale)};
-  a.ld = ((g.nkb + 15) / 16) * 16 + kLdsPad;
-  if (a.ld < 128) a.ld = 128;  // a row also holds the 256 radix counters of its selection
-  const int bh = p->batch * p->heads;
+  // the largest candidate union over the tiles of 4 rows, and over single rows (the fallback for
+  // unions beyond the LDS)
+  int max4 = 0, max1 = 0;
+  for (int r0 = 0; r0 < g.nqb; r0 += 4) {
+    const int u = tile_union(g, r0, g.nqb - r0 < 4 ? g.nqb - r0 : 4).size();
+    max4 = u > max4 ? u : max4;
+  }
+  for (int i = 0; i < g.nqb; ++i) {
+    const int u = tile_union(g, i, 1).size();
+    max1 = u > max1 ? u : max1;
+  }
+  SelArgs a{};
+  a.qp = q_pooled;
+  a.kp = k_pooled;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.dbg = scores_dbg;
+  a.g = g;
+  a.nnz = nnz;
+  a.bh = p->batch * p->heads;
+  a.scale = static_cast<double>(p->scale);
+  a.div_bpt = make_fastdiv(static_cast<uint32_t>(g.bpt));
+  a.div_wb = make_fastdiv(static_cast<uint32_t>(g.Wb));
+  // validate_problem bounds B * Hh * nkb by 2^30, so B * Hh * nqb workgroups fit an int
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const int slots = (g.nkb + 63) / 64;
-  if (p->head_dim == 128) {
-    if (slots <= 4) st = launch_rows<128, 4>(a, g, bh, s);
-    else if (slots <= 8) st = launch_rows<128, 8>(a, g, bh, s);
-    else if (slots <= 16) st = launch_rows<128, 16>(a, g, bh, s);
-    else st = launch_rows<128, kMaxSlots>(a, g, bh, s);
-  } else {
-    if (slots <= 4) st = launch_rows<64, 4>(a, g, bh, s);
-    else if (slots <= 8) st = launch_rows<64, 8>(a, g, bh, s);
-    else if (slots <= 16) st = launch_rows<64, 16>(a, g, bh, s);
-    else st = launch_rows<64, kMaxSlots>(a, g, bh, s);
-  }
+  const bool four = lds_need(4, max4) <= size_t(kLdsBytes);
+  if (!four && lds_need(1, max1) > size_t(kLdsBytes))
+    return fail(LCSA_ERR_UNSUPPORTED, "lcsa_score_select: %d candidate key blocks for one query block exceed the %d "
+                "that LDS holds", max1, kLdsBytes / 8 - 18);
+  if (p->head_dim == 128) st = four ? launch_slots<128, 4>(a, max4, s) : launch_slots<128, 1>(a, max1, s);
+  else st = four ? launch_slots<64, 4>(a, max4, s) : launch_slots<64, 1>(a, max1, s);
   if (st != LCSA_OK) return st;
   return hip_status(hipGetLastError(), "lcsa_score_select launch");
 }

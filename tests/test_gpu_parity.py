@@ -68,6 +68,23 @@ def test_clip_768x1408_26f():
     report(w.name, stats)
 
 
+# Beyond the former 1,248-key-block row limit: a 12-frame K/V cache at 1536x2688 with the 72-token
+# truncated window (1,512 key blocks, at most 6 x 81 candidates per query block), and a 40-frame cache
+# at 768x1408 without a window (1,320 key blocks, all of them candidates).
+LONG = [
+    W.Workload("uhd_1536x2688_kv12_win72_truncated", 1, 12, 128, 96, 168, 12, 10, 2, win_mode=1, win_h=72,
+               win_w=72, keep_ratio=W.RHO),
+    W.Workload("chunk_768x1408_kv40", 1, 12, 128, 48, 88, 40, 38, 2, keep_ratio=W.RHO),
+]
+
+
+@pytest.mark.parametrize("w", LONG, ids=lambda w: w.name)
+def test_long_caches(w):
+    assert w.nkb > 1248
+    stats = full_check(w, 0, qblocks=sample_blocks(w, 8), bh=[(0, h) for h in (0, 6, 11)])
+    report(w.name, stats)
+
+
 def test_full_selection_is_dense_block_causal():
     """keep ratio 1 on the GPU equals the oracle's dense masked attention (no selection)."""
     w = W.Workload("dense_small", 1, 2, 128, 24, 32, 6, 0, 6, keep_ratio=1.0)

@@ -161,9 +161,12 @@ def test_bad_pointers_and_strides_rejected_on_host():
         assert lib.lcsa_attn_fwd(ctypes.byref(pp), buf, good, buf, good, buf, good, buf, buf, buf, os_, None,
                                  None) == lcsa.LCSA_ERR_INVALID, (os_.batch, os_.head, os_.token)
         assert b"overlap" in lib.lcsa_last_error()
-    big = BASE.replace(kv_frames=40, q_frame0=38)            # 1320 key blocks > one LDS row
-    pb = lcsa.problem(big)
-    assert lib.lcsa_score_select(ctypes.byref(pb), buf, buf, buf, buf, None, None) == lcsa.LCSA_ERR_UNSUPPORTED
+    # one query block whose candidates outnumber what LDS holds (a 200-frame cache at 1536x2688 with no
+    # window: 25,200 candidate key blocks) is rejected; 40 frames at 768x1408 (1,320) are not
+    huge = BASE.replace(grid_h=96, grid_w=168, kv_frames=200, q_frame0=198)
+    ph = lcsa.problem(huge)
+    assert lib.lcsa_score_select(ctypes.byref(ph), buf, buf, buf, buf, None, None) == lcsa.LCSA_ERR_UNSUPPORTED
+    assert b"exceed" in lib.lcsa_last_error()
 
 
 def test_backward_rejections_on_host():

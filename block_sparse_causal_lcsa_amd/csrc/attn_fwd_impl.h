@@ -201,10 +201,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
 
   const Geom& g = a.g;
-  // XCD-aware order: hardware deals workgroup n to XCD n % 8; give each XCD a contiguous range
-  int wg = blockIdx.x;
-  const int n8 = (a.nwg / 8) * 8;
-  if (wg < n8) wg = (wg % 8) * (a.nwg / 8) + wg / 8;
+  const int wg = xcd_work_order(blockIdx.x, a.nwg, 1, g.nqb, g.nqb > g.bpt);  // one query block each
   const int bh = wg / g.nqb, i = wg - (wg / g.nqb) * g.nqb;
   const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
 
@@ -790,11 +787,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t v10[TE];
   __shared__ __attribute__((aligned(16))) uint16_t v11[TE];
 
-  // XCD-aware order over workgroups (hardware deals workgroup n to XCD n % 8)
-  const int nwg = a.nwg;
-  int wg = blockIdx.x;
-  const int n8 = (nwg / 8) * 8;
-  if (wg < n8) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int wg = xcd_work_order(blockIdx.x, a.nwg, 2, a.g.nqb, a.g.nqb > a.g.bpt);  // two query blocks each
   const int nblocks = a.nrows;
   const int q0 = 2 * wg, q1 = 2 * wg + 1;
   const const_i32* rp = (const const_i32*)(a.row_ptr);

@@ -208,6 +208,34 @@ LCSA_HD bool block_seen_whole(const Geom& g, int qhb, int qwb, int hb, int wb) {
   return kBlkW * wb >= lo_last && kBlkW * wb + kBlkW - 1 <= hi_first;
 }
 
+// Order of workgroups that each take `rows_per_wg` consecutive rows of the (batch, head)-major query
+// blocks (`nqb` per head). Hardware deals workgroup n to XCD n % 8 (local index n / 8). Each XCD
+// takes a contiguous range of the work, as equal in length as the count allows, so the workgroups that
+// share a head's K and V share one L2. Within its range an XCD starts at the first head boundary when
+// the part from there on is at least as long as the head tail before it, and wraps round to that tail:
+// the workgroups that start together then come from one head. With `descending`, each head's piece is
+// walked from its last row back: under the causal mask later rows keep more key blocks, so the long
+// workgroups start first and the short ones fill the end.
+LCSA_HD int xcd_work_order(int n, int nwg, int rows_per_wg, int nqb, bool descending) {
+  const int x = n % 8, l = n / 8;
+  const int q = nwg / 8, rem = nwg % 8;
+  const int c = q + (x < rem ? 1 : 0);
+  const int s = x * q + (x < rem ? x : rem);
+  const int rb = ((rows_per_wg * s + nqb - 1) / nqb) * nqb;  // first head-start row at or after s
+  int b = (rb + rows_per_wg - 1) / rows_per_wg;               // the workgroup holding it
+  if (b > s + c) b = s + c;
+  const int off = (s + c - b >= b - s) ? b - s : 0;
+  const int k = off + l;
+  const int g0 = s + (k >= c ? k - c : k);
+  if (!descending) return g0;
+  // mirror g0 inside its piece of one head: [b, s + c) or [s, b), cut at head boundaries
+  const int h = (rows_per_wg * g0) / nqb;
+  const int hs = (h * nqb + rows_per_wg - 1) / rows_per_wg, he = ((h + 1) * nqb + rows_per_wg - 1) / rows_per_wg;
+  const int lo = g0 >= b ? (hs > b ? hs : b) : (hs > s ? hs : s);
+  const int hi = g0 >= b ? (he < s + c ? he : s + c) : (he < b ? he : b);
+  return lo + hi - 1 - g0;
+}
+
 LCSA_HD int n_visible(const Geom& g, int i) {
   int h0, h1, w0, w1;
   const int tb = qblock_window(g, i, &h0, &h1, &w0, &w1);

@@ -52,6 +52,19 @@ def traffic_from_profile(workload: str):
     return float(t.group(1))
 
 
+def cold_leg(reps, cold_pool, cold_sel, pool_bytes, sel_bytes):
+    """The cold-cache figures, or None when the leg was skipped (--cold-reps 0)."""
+    import numpy as np
+    if not reps:
+        return None
+    mp, ms = float(np.median(cold_pool)), float(np.median(cold_sel))
+    return {"flush": "read sweep of 1 GiB before each timed call", "reps": reps,
+            "lcsa_pool_ms_median": round(mp, 4), "lcsa_score_select_ms_median": round(ms, 4),
+            "pool_gbs_cold": round(pool_bytes / (mp * 1e-3) / 1e9, 1),
+            "pool_frac_of_hbm_peak": round(pool_bytes / (mp * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "score_select_gbs_cold": round(sel_bytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def settle(run, seconds: float) -> float:
     """Untimed steps until at least `seconds` of wall time have passed (synchronising every 10 steps),
     so that clocks and caches reach their steady state whatever --warmup says. Returns the time spent."""
@@ -295,12 +308,7 @@ def main():
                            "lcsa_attn_fwd": pct(t_attn, 90), "step_events": pct(t_step_ev, 90)},
         "pool_gbs": round(pool_bytes / (med(t_pool) * 1e-3) / 1e9, 1),
         "score_select_gbs": round(sel_bytes / (med(t_sel) * 1e-3) / 1e9, 1),
-        "cold_cache": {"flush": "read sweep of 1 GiB before each timed call", "reps": args.cold_reps,
-                       "lcsa_pool_ms_median": round(med(cold_pool), 4),
-                       "lcsa_score_select_ms_median": round(med(cold_sel), 4),
-                       "pool_gbs_cold": round(pool_bytes / (med(cold_pool) * 1e-3) / 1e9, 1),
-                       "pool_frac_of_hbm_peak": round(pool_bytes / (med(cold_pool) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                       "score_select_gbs_cold": round(sel_bytes / (med(cold_sel) * 1e-3) / 1e9, 1)},
+        "cold_cache": cold_leg(args.cold_reps, cold_pool, cold_sel, pool_bytes, sel_bytes),
         "roofline": {"bound": "mfma", "kernel": "lcsa_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "flop_per_launch": flop, "avg_launch_ms": round(attn_ms, 4),

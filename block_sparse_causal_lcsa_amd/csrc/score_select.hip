@@ -78,6 +78,19 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// Maximum of x over the wave: row shifts give each lane the maximum of its row so far, the broadcasts of
+// lanes 15 and 31 carry it across rows, and lane 63 ends with the whole wave's maximum. Lanes whose
+// source lies outside the row take 0, the identity.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x111, 0xf, 0xf, false)));  // row_shr:1
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x112, 0xf, 0xf, false)));  // row_shr:2
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x114, 0xf, 0xf, false)));  // row_shr:4
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x118, 0xf, 0xf, false)));  // row_shr:8
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x142, 0xa, 0xf, false)));  // row_bcast:15
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x143, 0xc, 0xf, false)));  // row_bcast:31
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
 // floor(u / d) for 0 <= u < 2^22 and 1 <= d, with rcp = 1.0f / d: the float product is within 1/2 of
 // the quotient, so one correction either way makes it exact.
 __device__ __forceinline__ int udiv_small(int u, int d, float rcp) {
@@ -191,18 +204,25 @@ __global__ __launch_bounds__(64 * kRows) void score_select_kernel(SelArgs a) {
 #pragma unroll
     for (int v = 0; v < KR / 4; ++v) qf[v] = src[v];
   }
-  // each row's own window (candidate test when the scores are stored) and the tile's union
+  // each row's own window (candidate test when the scores are stored) and the tile's union: lane r
+  // works out row r0 + r (lanes past the tile repeat its first row), the rows are then read back
   int tbi[kRows], h0[kRows], h1[kRows], w0[kRows], w1[kRows];
   Union un{0, 1 << 30, 0, 1 << 30, 0};
   {
+    const uint32_t ir = uint32_t(r0 + (lane < rows ? lane : 0));
+    const uint32_t tr = fast_div(ir, a.div_bpt), rem = ir - tr * uint32_t(g.bpt);
+    const uint32_t hb = fast_div(rem, a.div_wb), wb = rem - hb * uint32_t(g.Wb);
+    int lh0, lh1, lw0, lw1;
+    qblock_window_at(g, int(hb), int(wb), &lh0, &lh1, &lw0, &lw1);
+    const int ltb = g.q_tb0 + int(tr);
     int uh1 = -1, uw1 = -1;
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      const uint32_t ir = uint32_t(r0 + (r < rows ? r : 0));
-      const uint32_t tr = fast_div(ir, a.div_bpt), rem = ir - tr * uint32_t(g.bpt);
-      const uint32_t hb = fast_div(rem, a.div_wb), wb = rem - hb * uint32_t(g.Wb);
-      tbi[r] = g.q_tb0 + int(tr);
-      qblock_window_at(g, int(hb), int(wb), &h0[r], &h1[r], &w0[r], &w1[r]);
+      tbi[r] = __builtin_amdgcn_readlane(ltb, r);
+      h0[r] = __builtin_amdgcn_readlane(lh0, r);
+      h1[r] = __builtin_amdgcn_readlane(lh1, r);
+      w0[r] = __builtin_amdgcn_readlane(lw0, r);
+      w1[r] = __builtin_amdgcn_readlane(lw1, r);
       un.nt = max(un.nt, tbi[r] + 1);
       un.h0 = min(un.h0, h0[r]);
       un.w0 = min(un.w0, w0[r]);
@@ -302,8 +322,20 @@ __global__ __launch_bounds__(64 * kRows) void score_select_kernel(SelArgs a) {
   uint32_t th = 1, tl = 0;
   int ties = 0;
   if (need < ncand) {
+    // the high halves span [hmin, hmax]; the bisection starts from that range
+    uint32_t hmin = 1, hmax = ~0u;
+    if constexpr (SLOTS > 0) {
+      uint32_t mx = 0, mn = 0;  // mn holds ~(smallest candidate high half)
+#pragma unroll
+      for (int m = 0; m < SLOTS; ++m) {
+        mx = max(mx, rk.hi[m]);
+        mn = max(mn, rk.hi[m] ? ~rk.hi[m] : 0u);
+      }
+      hmax = wave_max(mx);
+      hmin = ~wave_max(mn);
+    }
     bool exact;
-    th = bisect(1u, ~0u, need, &exact,
+    th = bisect(hmin, hmax, need, &exact,
                 [&](uint32_t t) { return count_keys<SLOTS, 0>(rk, srow, U, lane, t, 0); });
     if (!exact) {
       const int above = th == ~0u ? 0 : count_keys<SLOTS, 0>(rk, srow, U, lane, th + 1, 0);

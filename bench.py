@@ -52,6 +52,20 @@ def traffic_from_profile(workload: str):
     return float(t.group(1))
 
 
+def mfma_busy_from_profile(workload: str):
+    """SQ_VALU_MFMA_BUSY_CYCLES over the SIMD cycles of lcsa_attn_fwd from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on different attention sources."""
+    path = os.path.join(ROOT, "profiles", f"lcsa_forward_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"attn_fwd \([^)]*\) ([0-9a-f]{16})", text)
+    m = re.search(r"== lcsa_attn_fwd.*?SQ_VALU_MFMA_BUSY_CYCLES / [^=]*= ([0-9.]+)", text, re.S)
+    if not h or not m or h.group(1) != kernel_hash():
+        return None
+    return float(m.group(1))
+
+
 def cold_leg(reps, cold_pool, cold_sel, pool_bytes, sel_bytes):
     """The cold-cache figures, or None when the leg was skipped (--cold-reps 0)."""
     import numpy as np
@@ -279,6 +293,21 @@ def main():
         cold_sel.append(e[2].elapsed_time(e[3]))
     del flush
 
+    # matrix-core probe: the dense bf16 MFMA rate this GPU sustains right now (every CU busy), beside
+    # which the attention kernel's rate is also given; the roofline's peak stays the published one
+    probe_wgs, probe_iters = 2048, 1000
+    sink = torch.empty(probe_wgs * 256, dtype=torch.float32, device=dev)
+    probe_ms, probe_flop = [], 0.0
+    for _ in range(6):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        probe_flop = lcsa.lcsa_mfma_probe(probe_wgs, probe_iters, sink, stream=stream)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        probe_ms.append(e[0].elapsed_time(e[1]))
+    probe_tflops = probe_flop / (float(np.median(probe_ms[1:])) * 1e-3) / 1e12
+    del sink
+
     out = {
         "metric": "LCSA fwd effective TFLOP/s on selected blocks + ms per 8-frame chunk",
         "value": round(flop / (ms_per_step * 1e-3) / 1e12, 2),
@@ -309,9 +338,14 @@ def main():
         "pool_gbs": round(pool_bytes / (med(t_pool) * 1e-3) / 1e9, 1),
         "score_select_gbs": round(sel_bytes / (med(t_sel) * 1e-3) / 1e9, 1),
         "cold_cache": cold_leg(args.cold_reps, cold_pool, cold_sel, pool_bytes, sel_bytes),
+        "mfma_probe": {"tflops": round(probe_tflops, 1), "frac_of_spec_peak": round(probe_tflops / PEAK_BF16_TFLOPS, 4),
+                       "workgroups": probe_wgs, "iters": probe_iters,
+                       "what": "back-to-back v_mfma_f32_32x32x16_bf16, operands in registers, workgroups of 4 waves"},
         "roofline": {"bound": "mfma", "kernel": "lcsa_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "flop_per_launch": flop, "avg_launch_ms": round(attn_ms, 4),
+                     "mfma_busy": mfma_busy_from_profile(w.name),
+                     "frac_of_probe": round(achieved / probe_tflops, 4),
                      "event_intervals": int(ta.size), "event_outliers_dropped": int((~keep).sum())},
     }
 

@@ -23,7 +23,7 @@ LCSA_BF16, LCSA_F32 = 0, 1
 EXPORTS = ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
            "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd", "lcsa_attn_bwd_noalloc",
            "lcsa_stream_state_size", "lcsa_stream_init", "lcsa_stream_reserve", "lcsa_stream_push",
-           "lcsa_stream_window", "lcsa_rope_qkv",
+           "lcsa_stream_window", "lcsa_rope_qkv", "lcsa_mfma_probe",
            "lcsa_status_string", "lcsa_last_error", "lcsa_version")
 
 
@@ -91,9 +91,10 @@ def load():
     lib.lcsa_stream_push.argtypes = [SP, vp, S, vp, S, vp]
     lib.lcsa_stream_window.argtypes = [SP, P, ctypes.POINTER(vp), ctypes.POINTER(S), ctypes.POINTER(vp),
                                        ctypes.POINTER(S), ctypes.POINTER(vp)]
+    lib.lcsa_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, ctypes.POINTER(ctypes.c_double), vp]
     for f in ("lcsa_csr_layout", "lcsa_pool", "lcsa_score_select", "lcsa_attn_fwd",
               "lcsa_attn_bwd_workspace_size", "lcsa_attn_bwd", "lcsa_attn_bwd_noalloc", "lcsa_stream_state_size", "lcsa_stream_init",
-              "lcsa_stream_reserve", "lcsa_stream_push", "lcsa_stream_window", "lcsa_rope_qkv"):
+              "lcsa_stream_reserve", "lcsa_stream_push", "lcsa_stream_window", "lcsa_rope_qkv", "lcsa_mfma_probe"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lcsa_status_string.argtypes = [ctypes.c_int]
     lib.lcsa_status_string.restype = ctypes.c_char_p
@@ -450,3 +451,16 @@ def lcsa_rope_qkv(p: LcsaProblem, rope: LcsaRope, qkv, frame0: int, q=None, k=No
                                 frame0, n // hw, _ptr(outs[0]), _strides(outs[0]), _ptr(outs[1]),
                                 _strides(outs[1]), _ptr(outs[2]), _strides(outs[2]), _stream(stream)))
     return tuple(outs)
+
+
+def lcsa_mfma_probe(workgroups: int, iters: int, sink, stream=None) -> float:
+    """Launches the matrix-core throughput probe (measurement support, not part of the method) on
+    `stream`; sink: fp32 device tensor of at least workgroups * 256 elements. Returns the FLOP the
+    launch executes."""
+    torch = _torch()
+    _on_device("sink", sink)
+    if sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() < workgroups * 256:
+        raise ValueError(f"sink must be a contiguous float32 device tensor of >= {workgroups * 256} elements")
+    flop = ctypes.c_double(0.0)
+    _check(load().lcsa_mfma_probe(workgroups, iters, _ptr(sink), ctypes.byref(flop), _stream(stream)))
+    return flop.value

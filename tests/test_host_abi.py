@@ -2,6 +2,7 @@
 matches the header, the host geometry (lcsa_csr_layout) agrees with the oracle's independently
 written enumeration, and invalid problems are rejected before any device work."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -15,12 +16,15 @@ from oracle import lcsa_oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lcsa.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lcsa_[a-z_]+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"\b(lcsa_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -362,3 +366,14 @@ def test_binding_rejects_host_tensors():
         lcsa.lcsa_attn_bwd(p, q, k, v, q, q, torch.zeros((1, 2, nq)), row_ptr, col)
     with pytest.raises(ValueError, match="device tensor"):
         lcsa.lcsa_rope_qkv(p, lcsa.LcsaRope(22, 20, 22, 10000.0), torch.zeros((1, nq, 3 * 2 * 64), dtype=torch.bfloat16), 2)
+
+
+def test_mfma_probe_rejects_bad_arguments_on_host():
+    lib = lcsa.load()
+    flop = ctypes.c_double(-1.0)
+    sink = ctypes.c_void_p(16)
+    for wg, it in ((0, 10), (1 << 21, 10), (4, 0), (4, 1 << 25)):
+        assert lib.lcsa_mfma_probe(wg, it, sink, ctypes.byref(flop), None) == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_mfma_probe(4, 10, None, ctypes.byref(flop), None) == lcsa.LCSA_ERR_INVALID
+    assert lib.lcsa_mfma_probe(4, 10, ctypes.c_void_p(18), ctypes.byref(flop), None) == lcsa.LCSA_ERR_INVALID
+    assert flop.value == -1.0  # nothing written before validation passes

@@ -14,7 +14,7 @@ from block_sparse_causal_lcsa_amd import inputs, lcsa
 from block_sparse_causal_lcsa_amd import workloads as W
 from oracle import lcsa_oracle as O
 
-from parity import check_attention, check_selection, full_check, run_gpu, to_device, from_device
+from parity import check_attention, check_pooled, check_selection, full_check, run_gpu, to_device, from_device
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +83,38 @@ def test_long_caches(w):
     assert w.nkb > 1248
     stats = full_check(w, 0, qblocks=sample_blocks(w, 8), bh=[(0, h) for h in (0, 6, 11)])
     report(w.name, stats)
+
+
+# Rows with more candidates than the selection's register slots hold (over 2,048: it rereads the row's
+# scores from LDS on every pass), and a tile whose four-row union would overflow LDS (over 5,118
+# candidates: single-row tiles). Pool and selection against the oracle; attention is unaffected by
+# the row length and covered above.
+BEYOND = [
+    W.Workload("chunk_768x1408_kv66_rows_in_lds", 1, 1, 128, 48, 88, 66, 64, 2, keep_ratio=W.RHO),
+    W.Workload("grid_8x8_kv10242_single_row_tiles", 1, 1, 64, 8, 8, 10242, 10240, 2, keep_ratio=0.01),
+]
+
+
+@pytest.mark.parametrize("w", BEYOND, ids=lambda w: w.name)
+def test_selection_beyond_register_slots(w):
+    x = inputs.make_inputs(w, 0, want=("q", "k"))
+    p = lcsa.problem(w)
+    nqb, nkb, nnz, rp = lcsa.lcsa_csr_layout(p)
+    assert int(np.max(np.diff(rp))) >= 1 and nkb > 2048
+    q, k = to_device(x["q"]), to_device(x["k"])
+    qp, kp = lcsa.lcsa_pool(p, q, k)
+    col = lcsa.lcsa_score_select(p, qp, kp, torch.from_numpy(rp).to("cuda"))
+    torch.cuda.synchronize()
+    gpu = dict(row_ptr=rp.astype(np.int64), col_idx=col.cpu().numpy().astype(np.int64))
+    vis = O.visible(w)
+    assert int(vis.sum(axis=1).max()) > 2048
+    qbar, kbar = O.pool(w, inputs.to_f64(x["q"]), "q"), O.pool(w, inputs.to_f64(x["k"]), "k")
+    check_pooled(w, qp.cpu().numpy(), qbar)
+    check_pooled(w, kp.cpu().numpy(), kbar)
+    s = O.block_scores(w, qbar, kbar, vis)
+    rp_o, col_o = O.select(w, s, vis)
+    near, swapped = check_selection(w, gpu, s, col_o, rp_o)
+    report(w.name, dict(near_tie_rows=near, swapped_rows=swapped))
 
 
 def test_full_selection_is_dense_block_causal():

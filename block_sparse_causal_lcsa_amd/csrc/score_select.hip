@@ -168,7 +168,7 @@ __device__ __forceinline__ uint32_t bisect(uint32_t lo, uint32_t hi, int need, b
   return lo;
 }
 
-template <int D, int kRows, int SLOTS>
+template <int D, int kRows, int SLOTS, bool WIDE>
 __global__ __launch_bounds__(64 * kRows) void score_select_kernel(SelArgs a) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   extern __shared__ double S[];  // [kRows][a.ld] scores
@@ -260,12 +260,32 @@ __global__ __launch_bounds__(64 * kRows) void score_select_kernel(SelArgs a) {
       const int ct = wave + kRows * (n + p);
       if (ct >= nct) break;
       double acc[4] = {0.0, 0.0, 0.0, 0.0};  // four independent chains, summed in a fixed order
+      if constexpr (WIDE) {
+        // the whole column tile is widened first, into registers of its own: widening each value just
+        // before its MFMA reuses one register pair, and an MFMA still reading it holds up the next
+        // widening, so the chains run one MFMA at a time (about 4x slower). It costs 64 registers,
+        // hence one wave per SIMD; launched only when every workgroup has a CU of its own.
+        double kd[KR];
 #pragma unroll
-      for (int v = 0; v < KR / 4; ++v) {
-        acc[0] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v], (double)kb[p][v].x, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 1], (double)kb[p][v].y, acc[1], 0, 0, 0);
-        acc[2] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 2], (double)kb[p][v].z, acc[2], 0, 0, 0);
-        acc[3] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 3], (double)kb[p][v].w, acc[3], 0, 0, 0);
+        for (int v = 0; v < KR / 4; ++v) {
+          kd[4 * v] = kb[p][v].x;
+          kd[4 * v + 1] = kb[p][v].y;
+          kd[4 * v + 2] = kb[p][v].z;
+          kd[4 * v + 3] = kb[p][v].w;
+        }
+#pragma unroll
+        for (int v = 0; v < KR / 4; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[e] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + e], kd[4 * v + e], acc[e], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int v = 0; v < KR / 4; ++v) {
+          acc[0] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v], (double)kb[p][v].x, acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 1], (double)kb[p][v].y, acc[1], 0, 0, 0);
+          acc[2] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 2], (double)kb[p][v].z, acc[2], 0, 0, 0);
+          acc[3] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 3], (double)kb[p][v].w, acc[3], 0, 0, 0);
+        }
       }
       if (ct + kRows * PF < nct) load_col(ct + kRows * PF, kb[p]);
       const double sc = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * a.scale;
@@ -381,26 +401,48 @@ __global__ __launch_bounds__(64 * kRows) void score_select_kernel(SelArgs a) {
 // not on every call, so that launches can be captured into a HIP graph.
 constexpr int kMaxDevices = 64;
 
+// Compute units of the current device (cached per device).
+int device_cus(int dev) {
+  static std::atomic<int> cus[kMaxDevices];
+  int n = cus[dev].load(std::memory_order_acquire);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 1 << 30;
+    cus[dev].store(n, std::memory_order_release);
+  }
+  return n;
+}
+
+template <int D, int kRows, int SLOTS, bool WIDE>
+lcsa_status launch_one(SelArgs a, size_t lds, int dev, hipStream_t s) {
+  static std::atomic<uint64_t> raised[kMaxDevices];
+  if (raised[dev].load(std::memory_order_acquire) == 0) {
+    const lcsa_status st =
+        hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<D, kRows, SLOTS, WIDE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes),
+                   "lcsa_score_select LDS size");
+    if (st != LCSA_OK) return st;
+    raised[dev].store(1, std::memory_order_release);
+  }
+  score_select_kernel<D, kRows, SLOTS, WIDE><<<a.nwg, 64 * kRows, lds, s>>>(a);
+  return LCSA_OK;
+}
+
 template <int D, int kRows, int SLOTS>
 lcsa_status launch(SelArgs a, int max_union, hipStream_t s) {
-  static std::atomic<uint64_t> raised[kMaxDevices];
   int dev = 0;
   lcsa_status st = hip_status(hipGetDevice(&dev), "lcsa_score_select device");
   if (st != LCSA_OK) return st;
   if (dev < 0 || dev >= kMaxDevices) return fail(LCSA_ERR_UNSUPPORTED, "lcsa_score_select: device %d", dev);
-  if (raised[dev].load(std::memory_order_acquire) == 0) {
-    st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<D, kRows, SLOTS>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes),
-                    "lcsa_score_select LDS size");
-    if (st != LCSA_OK) return st;
-    raised[dev].store(1, std::memory_order_release);
-  }
   a.ld = ((max_union + 15) / 16) * 16 + 2;  // the pad spreads the 4 rows of a store over the banks
   const size_t lds = size_t(kRows) * a.ld * sizeof(double);
   a.tiles = (a.g.nqb + kRows - 1) / kRows;
   a.nwg = a.bh * a.tiles;
-  score_select_kernel<D, kRows, SLOTS><<<a.nwg, 64 * kRows, lds, s>>>(a);
-  return LCSA_OK;
+  // the widened-tile form when the grid is one workgroup per CU or less (small problems, where the
+  // scoring chain is the critical path); otherwise two workgroups per CU matter more
+  if constexpr (kRows == 4 && SLOTS > 0 && SLOTS <= 8) {
+    if (a.nwg <= device_cus(dev)) return launch_one<D, kRows, SLOTS, true>(a, lds, dev, s);
+  }
+  return launch_one<D, kRows, SLOTS, false>(a, lds, dev, s);
 }
 
 // Register slots of 64 candidates for the longest row: 4, 8, 16 or 32; beyond 2048 candidates the

@@ -279,12 +279,24 @@ __global__ __launch_bounds__(64 * kRows) void score_select_kernel(SelArgs a) {
           for (int e = 0; e < 4; ++e)
             acc[e] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + e], kd[4 * v + e], acc[e], 0, 0, 0);
       } else {
+        // half a tile at a time (32 registers), so two workgroups still fit a CU
 #pragma unroll
-        for (int v = 0; v < KR / 4; ++v) {
-          acc[0] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v], (double)kb[p][v].x, acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 1], (double)kb[p][v].y, acc[1], 0, 0, 0);
-          acc[2] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 2], (double)kb[p][v].z, acc[2], 0, 0, 0);
-          acc[3] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * v + 3], (double)kb[p][v].w, acc[3], 0, 0, 0);
+        for (int half = 0; half < 2; ++half) {
+          double kd[KR / 2];
+#pragma unroll
+          for (int v = 0; v < KR / 8; ++v) {
+            const float4 f = kb[p][half * (KR / 8) + v];
+            kd[4 * v] = f.x;
+            kd[4 * v + 1] = f.y;
+            kd[4 * v + 2] = f.z;
+            kd[4 * v + 3] = f.w;
+          }
+#pragma unroll
+          for (int v = 0; v < KR / 8; ++v)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[e] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[4 * (half * (KR / 8) + v) + e], kd[4 * v + e], acc[e],
+                                                          0, 0, 0);
         }
       }
       if (ct + kRows * PF < nct) load_col(ct + kRows * PF, kb[p]);

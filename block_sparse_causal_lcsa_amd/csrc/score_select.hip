@@ -263,7 +263,7 @@ __global__ __launch_bounds__(64 * kRows) void score_select_kernel(SelArgs a) {
       if constexpr (WIDE) {
         // the whole column tile is widened first, into registers of its own: widening each value just
         // before its MFMA reuses one register pair, and an MFMA still reading it holds up the next
-        // widening, so the chains run one MFMA at a time (about 4x slower). It costs 64 registers,
+        // widening, so the chains run one MFMA at a time (about 3x slower). It costs 64 registers,
         // hence one wave per SIMD; launched only when every workgroup has a CU of its own.
         double kd[KR];
 #pragma unroll

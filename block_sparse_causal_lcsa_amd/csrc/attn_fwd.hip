@@ -47,14 +47,14 @@ extern "C" lcsa_status lcsa_attn_fwd(const lcsa_problem* p, const void* q, lcsa_
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (p->dtype == LCSA_BF16) {
-    a.nwg = (a.nrows + 1) / 2;  // two query blocks per workgroup
+    a.nwg = a.nrows;  // one query block per workgroup
     const bool ragged = (g.H % kBlkH) != 0 || (g.W % kBlkW) != 0;
     const int mask = token_window(g) ? kMaskWindow : (ragged ? kMaskRagged : kMaskNone);
     if (mask == kMaskWindow) {
-      if (p->head_dim == 128) attn_fwd_pp_kernel<128, kMaskWindow><<<a.nwg, 512, 0, s>>>(a);
-      else attn_fwd_pp_kernel<64, kMaskWindow><<<a.nwg, 512, 0, s>>>(a);
+      if (p->head_dim == 128) attn_fwd_bf16_kernel<128, kMaskWindow><<<a.nwg, 256, 0, s>>>(a);
+      else attn_fwd_bf16_kernel<64, kMaskWindow><<<a.nwg, 256, 0, s>>>(a);
     } else {
-      launch_attn_fwd_pp_block(a, p->head_dim, mask == kMaskRagged, s);
+      launch_attn_fwd_bf16_block(a, p->head_dim, mask == kMaskRagged, s);
     }
   } else {
     if (p->head_dim == 128) attn_fwd_kernel<float, 128><<<a.nwg, 256, 0, s>>>(a);

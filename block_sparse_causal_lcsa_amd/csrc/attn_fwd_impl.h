@@ -12,8 +12,8 @@
 // Workgroup ids are remapped so that consecutive query blocks of one head run on the same XCD,
 // whose L2 then serves the key blocks that neighbouring query blocks share.
 //
-//  - bf16 (attn_fwd_pp_kernel): 8 waves per workgroup, two query blocks, K/V tiles loaded
-//    directly into LDS, matrix and vector phases of the two blocks interleaved ("ping-pong").
+//  - bf16 (attn_fwd_bf16_kernel): 4 waves per workgroup and query block, two workgroups per CU,
+//    K/V tiles loaded directly into LDS; each wave alternates a matrix phase and a vector phase.
 //  - fp32 inputs (attn_fwd_kernel): 4 waves per workgroup and query block; tiles are staged through
 //    registers, where fp32 is rounded to bf16.
 #pragma once
@@ -48,10 +48,10 @@ struct AttnArgs {
   int32_t nrows;            // (batch, head, query block) rows = B * Hh * nqb
 };
 
-// Launches the bf16 ping-pong kernel for block-granular masks (whole blocks, or partial edge blocks
+// Launches the bf16 kernel for block-granular masks (whole blocks, or partial edge blocks
 // when `ragged`; head_dim 64 or 128); defined in attn_fwd_block.hip, which is compiled with a
 // different instruction scheduler.
-void launch_attn_fwd_pp_block(const AttnArgs& a, int head_dim, bool ragged, hipStream_t s);
+void launch_attn_fwd_bf16_block(const AttnArgs& a, int head_dim, bool ragged, hipStream_t s);
 
 namespace {
 
@@ -441,16 +441,16 @@ __device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[2]) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Ping-pong schedule (bf16). A workgroup of 8 waves owns two query blocks: waves 0-3 (group 0) the
-// first, waves 4-7 (group 1) the second; wave w and wave w+4 share a SIMD. Time is cut into phases
-// that end at workgroup barriers. In every phase one group runs its matrix phase (P V of the
-// previous sub-block and Q K^T of the current one: 32 MFMAs per wave) while the other runs its
-// vector phase (row max, exponentials, row sums of the current sub-block), and the roles swap at
-// the next barrier, so each SIMD always has one wave feeding the matrix core and one on the vector
-// ALU. Group 1 starts one phase late.
-// Per group, M(m) reads K(m) and V(m-1) from LDS; the vector phase V(m) issues the direct-to-LDS
-// loads of K(m+2) and V(m+1) (their buffers were last read in M(m)) and, at its end, waits for the
-// loads of K(m+1) and V(m), issued one vector phase earlier, which M(m+1) reads.
+// Phase schedule (bf16). A workgroup of 4 waves owns one query block, and two workgroups share a CU,
+// so each SIMD runs one wave of each. A wave alternates a matrix phase (P V of the previous sub-block
+// and Q K^T of the current one: 32 MFMAs) and a vector phase (exponentials, bf16 packing and row
+// sums of the current sub-block); phases end at workgroup barriers. The two waves of a SIMD are not
+// locked to each other: vector work of one wave does not overlap the other's MFMAs on this hardware
+// (measured), so a ping-pong lock of two query blocks (one wave in each phase at every moment) only
+// adds barrier waits.
+// M(m) reads K(m) and V(m-1) from LDS; the vector phase V(m) issues the direct-to-LDS loads of K(m+2)
+// and V(m+1) (their buffers were last read in M(m)) and, at its end, waits for the loads of K(m+1)
+// and V(m), issued one vector phase earlier, which M(m+1) reads.
 typedef const __attribute__((address_space(4))) int32_t const_i32;
 
 // Barrier between phases without a memory fence: the direct-to-LDS loads in flight stay in flight.
@@ -481,7 +481,7 @@ __device__ __forceinline__ void wait_tiles(int n) {
 constexpr int kMaskNone = 0, kMaskRagged = 1, kMaskWindow = 2;
 
 template <int D, int MASK>
-__device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int row_start, int nsel, int nsel_other, int lwave,
+__device__ __forceinline__ void attn_group(const AttnArgs& a, int qblk, int row_start, int nsel, int lwave,
                                          uint16_t* kb0, uint16_t* kb1, uint16_t* vb0, uint16_t* vb1) {
   constexpr int DS = D / 16;
   constexpr int DT = D / 32;
@@ -491,12 +491,8 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int t = 2 * nsel;
-  const int t_other = 2 * nsel_other;
-  const int phases = 2 * (t > t_other ? t : t_other) + 2;  // common phase count of both groups
-  int phase = 0;
 
-  const bool has = qblk >= 0;
-  const int bh = has ? qblk / g.nqb : 0, i = has ? qblk - bh * g.nqb : 0;
+  const int bh = qblk / g.nqb, i = qblk - bh * g.nqb;
   const int b = bh / a.heads, h = bh - (bh / a.heads) * a.heads;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + b * a.qsb + h * a.qsh;
   const uint16_t* kbp = static_cast<const uint16_t*>(a.k) + b * a.ksb + h * a.ksh;
@@ -521,7 +517,7 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
   }
 
   bf16x8 qf[DS];
-  if (has) {
+  {
     const uint16_t* src = qb + int64_t(qtok) * a.qst + 8 * hi;
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
@@ -531,7 +527,7 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbp, a.k_span), vrs = make_rsrc(vbp, a.v_span);
   // the column list is read-only for the whole launch: read it through the scalar cache (uniform
   // scalar loads, which leave the vector-memory counter to the tile loads)
-  const const_i32* sel = (const const_i32*)(a.col_idx) + int64_t(bh) * a.nnz + (has ? row_start : 0);
+  const const_i32* sel = (const const_i32*)(a.col_idx) + int64_t(bh) * a.nnz + row_start;
   const uint32_t hw = uint32_t(g.H) * uint32_t(g.W);
   // first token of kept block j; ok: j is a block; lim: 16 * rows + cols inside the grid (136: full)
   auto block_base = [&](int j, bool& ok, int& lim) -> uint32_t {
@@ -572,10 +568,6 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   phase_barrier();
-  if (G == 1) {
-    phase_barrier();
-    ++phase;
-  }
 
   f32x16 S[2];
   bf16x8 pf[2][2];
@@ -717,10 +709,8 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
     vphase(ok_c, lim_c);
     wait_tiles<LOADS>(MORE ? 2 : 1);  // K(n, 1) and V(n, 0) have landed
     phase_barrier();
-    ++phase;
     mphase(vb0, kb1, Yes{}, Yes{});  // P V(n, 0); S = K(n, 1) Q^T
     phase_barrier();
-    ++phase;
     // ---- vector phase of m = 2n + 1
     if constexpr (MORE) {
       issue_tile<D, false>(krs, kb1, kst, base_n + hw, g.W, lwave, lane);  // K(n+1, 1)
@@ -729,14 +719,12 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
     vphase(ok_c, lim_c);
     wait_tiles<LOADS>(MORE ? 2 : 0);  // K(n+1, 0) and V(n, 1) have landed
     phase_barrier();
-    ++phase;
     if constexpr (MORE) {
       mphase(vb1, kb0, Yes{}, Yes{});  // P V(n, 1); S = K(n+1, 0) Q^T
     } else {
       mphase(vb1, kb0, Yes{}, No{});
     }
     phase_barrier();
-    ++phase;
     ok_c = ok_n;
     lim_c = lim_n;
     base_c = base_n;
@@ -747,16 +735,11 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
   if (t > 0) {
     mphase(vb1, kb0, No{}, Yes{});  // M(0): S = K(0, 0) Q^T
     phase_barrier();
-    ++phase;
     for (int n = 0; n + 1 < nsel; ++n) block_iter(n, Yes{});
     block_iter(nsel - 1, No{});
   }
-  while (phase < phases) {
-    phase_barrier();
-    ++phase;
-  }
 
-  if (!has || !q_in) return;  // no query block, or a query row outside the grid
+  if (!q_in) return;  // a query row outside the grid (partial block) has no output
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   uint16_t* ob = static_cast<uint16_t*>(a.o) + b * a.osb + h * a.osh + int64_t(qtok) * a.ost;
@@ -776,30 +759,18 @@ __device__ __forceinline__ void pp_group(const AttnArgs& a, int G, int qblk, int
 }
 
 template <int D, int MASK>
-__global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int TE = Tile<D>::ELEMS;
-  __shared__ __attribute__((aligned(16))) uint16_t k00[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t k01[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t v00[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t v01[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t k10[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t k11[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t v10[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t v11[TE];
-
-  const int wg = xcd_work_order(blockIdx.x, a.nwg, 2, a.g.nqb, a.g.nqb > a.g.bpt);  // two query blocks each
-  const int nblocks = a.nrows;
-  const int q0 = 2 * wg, q1 = 2 * wg + 1;
+  __shared__ __attribute__((aligned(16))) uint16_t k0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t k1[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t v0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t v1[TE];
+  const int qblk = xcd_work_order(blockIdx.x, a.nwg, 1, a.g.nqb, a.g.nqb > a.g.bpt);  // one query block each
   const const_i32* rp = (const const_i32*)(a.row_ptr);
-  const int i0 = q0 % a.g.nqb, i1 = q1 % a.g.nqb;
-  const int r0 = rp[i0], n0 = rp[i0 + 1] - r0;
-  const int r1 = q1 < nblocks ? rp[i1] : 0, n1 = q1 < nblocks ? rp[i1 + 1] - r1 : 0;
-  const int G = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
-  const int lwave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);
-  if (G == 0)
-    pp_group<D, MASK>(a, 0, q0, r0, n0, n1, lwave, k00, k01, v00, v01);
-  else
-    pp_group<D, MASK>(a, 1, q1 < nblocks ? q1 : -1, r1, n1, n0, lwave, k10, k11, v10, v11);
+  const int i = qblk % a.g.nqb;
+  const int r0 = rp[i], n = rp[i + 1] - r0;
+  const int lwave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  attn_group<D, MASK>(a, qblk, r0, n, lwave, k0, k1, v0, v1);
 }
 
 }  // namespace

@@ -643,11 +643,12 @@ __device__ __forceinline__ void attn_group(const AttnArgs& a, int qblk, int row_
         for (int e = 0; e < 8; ++e) pf[kt][h2][e] = (__bf16)x[kt][8 * h2 + e];
     // row sum of the fp32 probabilities, before their rounding to bf16: the denominator (and lse)
     // stay exact to fp32 even when one rounded probability carries most of a row's mass
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    // (the chains start at the first four values: the same sums as from 0, without four adds)
+    float acc[4] = {x[0][0], x[0][1], x[0][2], x[0][3]};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v & 3] += x[kt][v];
+      for (int v = kt == 0 ? 4 : 0; v < 16; ++v) acc[v & 3] += x[kt][v];
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
   auto vphase = [&](bool ok, int lim) __attribute__((always_inline)) {
